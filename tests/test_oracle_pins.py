@@ -1,0 +1,305 @@
+"""Pins of the oracle against library routines, closed forms, limits,
+invariants and hand-worked cases (CPU only)."""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from workloads import Config, f32_to_bf16_bits, make_workload
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_bf16_widening_matches_torch():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(4096) * 30).astype(np.float32)
+    bits = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.widen(bits, "bf16"), ref)
+    # torch's own float32 -> bfloat16 rounding is round-to-nearest-even too
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, tb)
+
+
+# ---------------------------------------------------------------- softmax
+
+@pytest.mark.parametrize("tau", [0.3, 0.7, 1.0, 2.5])
+def test_softmax_matches_scipy_and_torch(tau):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(5000) * 3
+    p = oracle.softmax_temp(x, tau)
+    np.testing.assert_allclose(p, scipy.special.softmax(x / tau), rtol=1e-13, atol=0)
+    pt = torch.softmax(torch.from_numpy(x) / tau, dim=0).numpy()
+    np.testing.assert_allclose(p, pt, rtol=1e-12, atol=0)
+    assert abs(math.fsum(p) - 1) < 1e-14
+
+
+def test_softmax_shift_invariance_and_masking():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(1000)
+    np.testing.assert_allclose(oracle.softmax_temp(x, 0.8),
+                               oracle.softmax_temp(x + 17.25, 0.8), rtol=1e-12)
+    y = x.copy()
+    y[::3] = -np.inf
+    p = oracle.softmax_temp(y, 0.8)
+    assert np.all(p[::3] == 0)
+    q = scipy.special.softmax(x[np.isfinite(y)] / 0.8)
+    np.testing.assert_allclose(p[np.isfinite(y)], q, rtol=1e-13)
+
+
+def test_softmax_greedy_and_row_errors():
+    x = np.array([1.0, 3.0, 3.0, 2.0])
+    np.testing.assert_array_equal(oracle.softmax_temp(x, 0.0), [0, 1, 0, 0])
+    with pytest.raises(oracle.RowError):
+        oracle.softmax_temp(np.array([-np.inf, -np.inf]), 1.0)
+    with pytest.raises(oracle.RowError):
+        oracle.softmax_temp(np.array([0.0, np.inf]), 1.0)
+
+
+# ---------------------------------------------------------------- inverse CDF
+
+def test_inverse_cdf_matches_searchsorted():
+    """Token-id order and the 'first C_t > uZ' boundary, against numpy."""
+    rng = np.random.default_rng(4)
+    for _ in range(300):
+        V = int(rng.integers(1, 60))
+        w = rng.random(V)
+        w[rng.random(V) < 0.4] = 0.0
+        if w.sum() == 0:
+            w[int(rng.integers(V))] = 0.5
+        u = float(rng.integers(0, 2**24)) * 2.0**-24
+        tok, _ = oracle.inverse_cdf(w.tolist(), u)
+        c = np.cumsum(w)
+        ref = int(np.searchsorted(c, u * c[-1], side="right"))
+        if ref >= V:
+            ref = int(np.flatnonzero(w > 0)[-1])
+        assert tok == ref
+        assert w[tok] > 0
+
+
+def test_inverse_cdf_edges():
+    w = [0.0, 0.25, 0.0, 0.75, 0.0]
+    assert oracle.inverse_cdf(w, 0.0)[0] == 1
+    assert oracle.inverse_cdf(w, 0.2499)[0] == 1
+    assert oracle.inverse_cdf(w, 0.25)[0] == 3  # C_1/Z = 0.25 is not > 0.25
+    assert oracle.inverse_cdf(w, 1 - 2**-24)[0] == 3
+    # flags near a breakpoint
+    assert oracle.inverse_cdf(w, 0.25 - 5e-7)[1]
+    assert not oracle.inverse_cdf(w, 0.5)[1]
+
+
+# ---------------------------------------------------------------- greedy
+
+def test_greedy_is_prefix_match():
+    """Temperature 0 reduces to greedy verification: the accepted length is
+    the length of the common prefix of the drafts and the target argmaxes,
+    and the emitted token is the target argmax there."""
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        k, V = int(rng.integers(1, 6)), int(rng.integers(2, 7))
+        T = rng.integers(0, 3, (k + 1, V)).astype(np.float64)  # many ties
+        am = [min(t for t in range(V) if T[j, t] == T[j].max()) for j in range(k + 1)]
+        drafts = [am[j] if rng.random() < 0.6 else int(rng.integers(V)) for j in range(k)]
+        n = 0
+        while n < k and drafts[n] == am[n]:
+            n += 1
+        v = oracle.verify_greedy(list(T), drafts)
+        assert (v.accept_len, v.token) == (n, am[n])
+
+
+def test_small_temperature_limit_matches_greedy():
+    """As tau -> 0 the stochastic rule becomes the greedy one: with logits
+    separated by >= 1 and tau = 0.01 every probability other than the argmax
+    is below e^-100, far inside the flag band."""
+    rng = np.random.default_rng(6)
+    for _ in range(100):
+        k, V = 3, 6
+        T = np.stack([rng.permutation(V).astype(np.float64) for _ in range(k + 1)])
+        D = np.stack([rng.permutation(V).astype(np.float64) for _ in range(k + 1)])
+        am = T.argmax(1)
+        drafts = np.array([am[j] if rng.random() < 0.7 else D[j].argmax() for j in range(k)])
+        ua = rng.random(k) * 0.98 + 0.01
+        ur = rng.random(k + 1) * 0.98 + 0.01
+        g = oracle.verify_sequence(T, D, "f32", drafts, 0.0, ua, ur)
+        s = oracle.verify_sequence(T, D, "f32", drafts, 0.01, ua, ur)
+        assert (g.accept_len, g.token) == (s.accept_len, s.token)
+
+
+# ---------------------------------------------------------------- forks
+
+def test_forks_match_sorted_key():
+    rng = np.random.default_rng(7)
+    for _ in range(100):
+        V = int(rng.integers(2, 40))
+        y = rng.integers(-3, 4, V).astype(np.float64)
+        f = int(rng.integers(1, V))
+        ex = int(rng.integers(V)) if rng.random() < 0.8 else None
+        toks, _ = oracle.forked_topf(y, 1.0, f, ex)
+        ref = sorted((t for t in range(V) if t != ex), key=lambda t: (-y[t], t))[:f]
+        assert list(toks) == ref
+
+
+def test_fork_probs_are_masked_softmax():
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal(300) * 2
+    toks, probs = oracle.forked_topf(y, 0.7, 5, 17)
+    z = y.copy()
+    z[17] = -np.inf
+    ref = scipy.special.softmax(z / 0.7)
+    np.testing.assert_allclose(probs, ref[toks], rtol=1e-13)
+    toks0, probs0 = oracle.forked_topf(y, 0.0, 3, None)
+    np.testing.assert_array_equal(probs0, [1, 0, 0])
+
+
+# ---------------------------------------------------------------- residual
+
+def test_residual_distribution_properties():
+    rng = np.random.default_rng(9)
+    P = scipy.special.softmax(rng.standard_normal(500))
+    Q = scipy.special.softmax(rng.standard_normal(500))
+    r = oracle.residual_distribution(P, Q)
+    assert abs(r.sum() - 1) < 1e-14
+    assert np.all(r[P <= Q] == 0)
+    pos = P > Q
+    np.testing.assert_allclose(r[pos], (P - Q)[pos] / (P - Q)[pos].sum(), rtol=1e-12)
+    np.testing.assert_array_equal(oracle.residual_distribution(P, P), P)
+
+
+# ---------------------------------------------------------------- invariants
+
+def _small_zipf(B, k, V, tau, seed, f=3):
+    return make_workload(Config("t", B=B, k=k, V=V, f=f, dtype="bf16",
+                                profile="zipf", seed=seed, tau=tau,
+                                sigma_range=(0.3, 1.2)))
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.7, 1.3])
+def test_invariants_on_synthetic_batches(tau):
+    w = _small_zipf(12, 5, 3000, tau, 11)
+    r = oracle.verify_batch(w.target, w.draft, "bf16", w.draft_tokens,
+                            w.temperature, w.u_accept, w.u_recover, f=3)
+    assert np.all((r.accept_len >= 0) & (r.accept_len <= w.k))
+    for i in range(w.B):
+        n = r.accept_len[i]
+        if n < w.k:
+            assert r.token[i] != w.draft_tokens[i, n]  # rejected draft never re-emitted
+        for j in range(w.k + 1):
+            ft = list(r.fork_tokens[i, j])
+            assert len(set(ft)) == 3
+            if j < w.k:
+                assert w.draft_tokens[i, j] not in ft
+            y = oracle.widen(w.draft[i, j], "bf16")[ft]
+            assert np.all(np.diff(y) <= 0)
+            assert np.all(np.diff(r.fork_probs[i, j]) <= 0 if tau > 0 else True)
+
+
+def test_identical_drafter_accepts_everything():
+    w = _small_zipf(6, 4, 2000, 0.9, 12)
+    r = oracle.verify_batch(w.target, w.target, "bf16", w.draft_tokens,
+                            w.temperature, w.u_accept, w.u_recover)
+    assert np.all(r.accept_len == w.k)
+
+
+def test_disjoint_support_rejects_first():
+    V, k = 50, 3
+    T = np.full((k + 1, V), -np.inf)
+    D = np.full((k + 1, V), -np.inf)
+    T[:, :25] = 0.0
+    D[:, 25:] = 0.0
+    r = oracle.verify_sequence(T, D, "f32", [30, 31, 32], 1.0, [0.0] * k, [0.5] * (k + 1))
+    assert r.accept_len == 0 and r.token < 25
+    assert r.p_draft[0] == 0 and r.q_draft[0] == pytest.approx(1 / 25)
+
+
+def test_error_sequences():
+    T = np.zeros((3, 8))
+    D = np.zeros((3, 8))
+    assert oracle.verify_sequence(T, D, "f32", [1, 9], 1.0, [0.1, 0.1], [0.1] * 3).error
+    assert oracle.verify_sequence(T, D, "f32", [1, 2], -1.0, [0.1, 0.1], [0.1] * 3).error
+    assert oracle.verify_sequence(T, D, "f32", [1, 2], float("nan"), [0.1, 0.1], [0.1] * 3).error
+    T2 = T.copy()
+    T2[2] = -np.inf
+    assert oracle.verify_sequence(T2, D, "f32", [1, 2], 1.0, [0.1, 0.1], [0.1] * 3).error
+    # row k of the drafter is read only for forks
+    D2 = D.copy()
+    D2[2, 3] = np.inf
+    assert not oracle.verify_sequence(T, D2, "f32", [1, 2], 1.0, [0.1, 0.1], [0.1] * 3).error
+    assert oracle.verify_sequence(T, D2, "f32", [1, 2], 1.0, [0.1, 0.1], [0.1] * 3, f=2).error
+
+
+# ---------------------------------------------------------------- hand-worked
+
+LN = np.log
+
+
+def test_hand_worked_reject_then_residual():
+    """p0 = (1/2, 1/4, 1/4), q0 = (1/4, 1/2, 1/4), drafted token 1:
+    a = (1/4)/(1/2) = 1/2.  u = 0.75 >= 1/2 rejects at position 0; the
+    residual max(0, p - q) = (1/4, 0, 0) puts all its mass on token 0."""
+    T = np.array([[LN(.5), LN(.25), LN(.25)], [0.0, 0.0, 0.0]])
+    D = np.array([[LN(.25), LN(.5), LN(.25)], [0.0, 0.0, 0.0]])
+    r = oracle.verify_sequence(T, D, "f32", [1], 1.0, [0.75], [0.3, 0.9])
+    assert (r.accept_len, r.token) == (0, 0)
+    assert r.p_draft[0] == pytest.approx(0.25, rel=1e-6)
+    assert r.q_draft[0] == pytest.approx(0.5, rel=1e-6)
+
+
+def test_hand_worked_accept_then_bonus():
+    """Same position 0 with u = 0.25 < 1/2: accepted; the bonus token is
+    drawn from p1 = (0.1, 0.2, 0.7) with u = 0.35: C = (0.1, 0.3, 1.0), the
+    first C_t > 0.35 is t = 2."""
+    T = np.array([[LN(.5), LN(.25), LN(.25)], [LN(.1), LN(.2), LN(.7)]])
+    D = np.array([[LN(.25), LN(.5), LN(.25)], [0.0, 0.0, 0.0]])
+    r = oracle.verify_sequence(T.astype(np.float32), D.astype(np.float32), "f32",
+                               [1], 1.0, [0.25], [0.99, 0.35])
+    assert (r.accept_len, r.token) == (1, 2)
+
+
+def test_hand_worked_recover_uses_uniform_of_rejected_position():
+    """k = 2.  Position 0: p = q, accepted for any u.  Position 1:
+    p1 = (1/4, 1/2, 1/4), q1 = (0, 1/4, 3/4), drafted token 2:
+    a = (1/4)/(3/4) = 1/3, and u = 0.5 rejects.  The residual is
+    (1/4, 1/4, 0) with Z = 1/2, so C/Z = (0.5, 1, 1): u_recover[1] = 0.7
+    gives token 1, while the other entries (0.1) would give token 0."""
+    T = np.array([[0, 0, 0], [LN(.25), LN(.5), LN(.25)], [0, 0, 0]], dtype=np.float64)
+    D = np.array([[0, 0, 0], [-np.inf, LN(.25), LN(.75)], [0, 0, 0]], dtype=np.float64)
+    r = oracle.verify_sequence(T, D, "f32", [0, 2], 1.0, [0.9, 0.5], [0.1, 0.7, 0.1])
+    assert (r.accept_len, r.token) == (1, 1)
+
+
+def test_hand_worked_greedy_ties():
+    """tau = 0: target row (1, 3, 3, 2) has argmax 1 (lowest of the tie);
+    drafted token 2 is rejected and token 1 is emitted."""
+    T = np.array([[1, 3, 3, 2], [0, 0, 0, 0]], dtype=np.float64)
+    D = np.array([[0, 0, 5, 0], [0, 0, 0, 0]], dtype=np.float64)
+    r = oracle.verify_sequence(T, D, "f32", [2], 0.0, [0.0], [0.0, 0.0])
+    assert (r.accept_len, r.token) == (0, 1)
+    np.testing.assert_array_equal(r.p_draft, [0.0])
+    np.testing.assert_array_equal(r.q_draft, [1.0])
+
+
+def test_hand_worked_forks():
+    """Draft row (0.5, 2, 2, 1, 2), drafted token 1 masked, f = 3: order by
+    (-y, t) gives 2, 4, 3.  At tau = 1 their probabilities are e^2/S, e^2/S,
+    e/S with S = e^0.5 + 2e^2 + e (the masked row's softmax)."""
+    y = np.array([0.5, 2, 2, 1, 2])
+    toks, probs = oracle.forked_topf(y, 1.0, 3, 1)
+    assert list(toks) == [2, 4, 3]
+    S = math.exp(0.5) + 2 * math.exp(2) + math.exp(1)
+    np.testing.assert_allclose(probs, [math.exp(2) / S, math.exp(2) / S, math.e / S], rtol=1e-14)
+
+
+def test_sample_at_position_agrees_with_verify():
+    w = _small_zipf(8, 4, 2500, 0.8, 13, f=0)
+    r = oracle.verify_batch(w.target, w.draft, "bf16", w.draft_tokens,
+                            w.temperature, w.u_accept, w.u_recover)
+    for i in range(w.B):
+        tok, flag, _, err = oracle.sample_at_position(
+            w.target[i], w.draft[i], "bf16", w.draft_tokens[i],
+            w.temperature[i], r.accept_len[i], w.u_recover[i])
+        assert not err and tok == r.token[i]
