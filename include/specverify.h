@@ -1,0 +1,204 @@
+/*
+ * libspecverify -- the verify-and-speculate step of speculative decoding and
+ * of speculative speculative decoding (SSD), for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  No C++ or framework types cross it: plain pointers, sizes and the
+ * small structs below.  Unless stated otherwise every array pointer is a
+ * DEVICE pointer owned by the caller; the library allocates no memory of its
+ * own, keeps no global mutable state, launches only on the stream it is
+ * given (a hipStream_t passed as void*, NULL = the default stream) and
+ * returns before the work completes: results are valid once the caller has
+ * synchronised that stream.
+ *
+ * What is computed (sources are cited by page title and section):
+ *
+ *  - A small drafter proposes k tokens; the target scores all of them in one
+ *    forward pass, keeps the correct prefix and regenerates from the first
+ *    divergence ("How It Works", speculative-sampling project page,
+ *    sourcepulse.org project 1842340; "What changes in SSD", hysenlabs.com
+ *    editorial on SSD).  The rule is speculative sampling in its textbook
+ *    form (the same page names the Google and DeepMind variants under
+ *    "Highlighted Details"): accept drafted token d at position j iff
+ *    u < min(1, p_j(d) / q_j(d)); at the first rejection n emit a token drawn
+ *    by inverse CDF from the normalised residual max(0, p_n - q_n); if all k
+ *    are accepted emit a bonus token drawn from p_k.  The result is exact:
+ *    the emitted tokens follow the target distribution ("What changes in
+ *    SSD").
+ *  - p and q are the softmax of the logits at the sequence's temperature;
+ *    at temperature 0 the step is greedy (argmax, lowest id on ties), the
+ *    sampler's greedy/stochastic switch in the tanishqkumar/ssd repository
+ *    summary (thehardwarestore.ai, highlighted sampler file).
+ *  - SSD's forked recovery tokens: per position, the top-f draft tokens with
+ *    the drafted token masked out, so the drafter can pre-speculate every
+ *    likely verification outcome (same summary, highlighted async-SD
+ *    utilities file; f alternatives in the SSD README's benchmark commands,
+ *    m.111cn.net translation, section 基准测试).
+ *
+ * Shapes and layout.  B sequences, k drafted positions (1 <= k <= 63),
+ * positions j = 0..k where j = k is the bonus position, vocabulary V >= 2
+ * shared by target and drafter (speculative-sampling page, "Quick Start &
+ * Requirements": both models must share one vocabulary).  Logits are
+ * [B][k+1][V] with V contiguous, addressed with element strides; every row
+ * start must be 16-byte aligned (so strides must be multiples of 4 fp32 /
+ * 8 bf16 elements).  Uniforms are caller-supplied in [0, 1): the library
+ * holds no random-number state.
+ *
+ * Numerics.  Elementwise exponentials in fp32, per-row sums accumulated in
+ * fp32 within a lane and in fp64 across lanes and chunks, acceptance ratios
+ * and CDF prefixes in fp64.  Reductions have a fixed order: results are
+ * bitwise deterministic from run to run.
+ *
+ * Errors.  Host-detectable problems (null required pointers, sizes out of
+ * range, misaligned rows, unknown dtype, short workspace) return a status and
+ * launch nothing.  Problems visible only in device data make the affected
+ * sequence an error: a temperature that is NaN, negative or infinite, a
+ * drafted id outside [0, V), or a logits row that is read and whose maximum
+ * is not finite (+inf, or every entry -inf).  Such a sequence gets -1 in its
+ * integer outputs and NaN in its float outputs; nothing is read out of
+ * bounds.  NaN logits are outside the contract (results unspecified, still
+ * in bounds).
+ *
+ * Workspace.  Every compute call takes a device workspace of at least
+ * sv_workspace_size() bytes.  It must be zero-filled before its first use
+ * (sv_workspace_init, or any zero fill); every call leaves it zero-filled in
+ * the parts that must start at zero.  Calls that share a workspace must not
+ * overlap in time (use one workspace per stream).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = 1, /* null required pointer, size out of range, bad enum */
+  SV_ERR_MISALIGNED = 2,  /* a logits or output row does not start 16-byte aligned */
+  SV_ERR_WORKSPACE = 3,   /* workspace null or smaller than sv_workspace_size() */
+  SV_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* One batch of verify inputs.  target/draft: [B][k+1][V] logits of dtype
+ * `dtype` at the given element strides (row k of the draft is read only for
+ * forks; a draft of [B][k][V] may be passed with forks off).
+ * draft_tokens: [B][k] int32, contiguous.  temperature: [B] fp32; 0 =
+ * greedy. */
+typedef struct sv_batch {
+  int32_t B, k, V;
+  int32_t dtype; /* sv_dtype, same for target and draft */
+  const void* target;
+  int64_t t_seq_stride, t_row_stride;
+  const void* draft;
+  int64_t d_seq_stride, d_row_stride;
+  const int32_t* draft_tokens;
+  const float* temperature;
+} sv_batch;
+
+/* Forked recovery outputs: tokens [B][k+1][f] int32 (required), probs
+ * [B][k+1][f] fp32 (nullable), 1 <= f <= min(16, V-1).  Probabilities are
+ * the softmax at the sequence temperature of the draft logits with the
+ * drafted token masked out (nothing masked at j = k); (1, 0, ...) at
+ * temperature 0. */
+typedef struct sv_forks {
+  int32_t f;
+  int32_t* tokens;
+  float* probs;
+} sv_forks;
+
+/* Optional per-call extras.  ev_stats_begin / ev_stats_end: hipEvent_t
+ * handles (as void*) recorded on the call's stream immediately before and
+ * after the streaming statistics kernel, for timing it on its own; NULL =
+ * not recorded. */
+typedef struct sv_opts {
+  void* ev_stats_begin;
+  void* ev_stats_end;
+} sv_opts;
+
+/* Bytes of workspace any entry point needs for these sizes (an upper bound
+ * over dtypes).  For sv_softmax_temp pass B = rows, k = 0, f = 0.
+ * Returns 0 for sizes out of range. */
+size_t sv_workspace_size(int32_t B, int32_t k, int32_t V, int32_t f);
+
+/* Zero-fills `bytes` bytes of a workspace on `stream` with a fill kernel
+ * (no memset node, so it can be captured in a graph). */
+sv_status sv_workspace_init(void* ws, size_t bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* sv_status_string(int32_t status);
+
+/* Library version string (static storage). */
+const char* sv_version(void);
+
+/* Temperature softmax of `rows` logits rows:
+ * probs[r][t] = softmax(logits[r] / tau)[t] with tau = temperature[r /
+ * rows_per_temp]; one-hot at the first maximum when tau = 0.  logits: rows
+ * of V elements at row_stride elements; probs: fp32 rows at out_row_stride
+ * elements (16-byte aligned rows).  A row whose maximum is not finite, or
+ * whose temperature is invalid, comes back as NaN.  Reads the logits twice
+ * (statistics, then normalise-and-write). */
+sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows,
+                          int32_t V, int64_t row_stride,
+                          const float* temperature, int64_t rows_per_temp,
+                          float* probs, int64_t out_row_stride, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* The verify step, with the forked recovery tokens fused into the same pass
+ * over the draft logits when `forks` is non-NULL.
+ *   u_accept [B][k]    uniform of the acceptance test at each position
+ *   u_recover [B][k+1] uniform of the draw at the outcome position n
+ *   accept_len [B]     out: n = number of accepted drafted tokens, in [0, k]
+ *   out_token [B]      out: the recovery token (n < k) or bonus token (n = k)
+ *   p_draft, q_draft [B][k] out (nullable): p_j(d_j), q_j(d_j) (one-hot
+ *                      indicators at temperature 0).  Passing q_draft makes
+ *                      the draft rows be read also at temperature 0.
+ * Launches: statistics kernel (one wave per 4096-element chunk of a row,
+ * rows merged and sequences decided by the last wave to finish), then a
+ * residual kernel that re-reads only row n of the temperature > 0
+ * sequences. */
+sv_status sv_verify(const sv_batch* in, const float* u_accept,
+                    const float* u_recover, int32_t* accept_len,
+                    int32_t* out_token, float* p_draft, float* q_draft,
+                    const sv_forks* forks, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* sv_verify with extras (see sv_opts); opts may be NULL. */
+sv_status sv_verify_ex(const sv_batch* in, const float* u_accept,
+                       const float* u_recover, int32_t* accept_len,
+                       int32_t* out_token, float* p_draft, float* q_draft,
+                       const sv_forks* forks, void* ws, size_t ws_bytes,
+                       void* stream, const sv_opts* opts);
+
+/* The draw at a given position of each sequence, and optionally the full
+ * residual distributions.
+ *   position [B]   n in [0, k]: n < k draws from max(0, p_n - q_n)
+ *                  normalised (p_n if that is zero everywhere), n = k draws
+ *                  the bonus token from p_k; greedy at temperature 0
+ *   u_recover [B][k+1]; token_out [B] out
+ *   residual [B][k+1][V] fp32 out (nullable): for every position j < k the
+ *                  normalised residual, p_k at j = k, one-hot at the target
+ *                  argmax at temperature 0; rows at res_seq_stride /
+ *                  res_row_stride elements, 16-byte aligned.
+ * A position outside [0, k] makes that sequence an error. */
+sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,
+                             const float* u_recover, int32_t* token_out,
+                             float* residual, int64_t res_seq_stride,
+                             int64_t res_row_stride, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Forked recovery tokens alone, from the draft logits only (drafter-side
+ * use in SSD, where the drafter runs on its own device without the target's
+ * logits).  in->target may be NULL. */
+sv_status sv_forked_topf(const sv_batch* in, const sv_forks* forks, void* ws,
+                         size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

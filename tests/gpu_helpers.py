@@ -1,0 +1,110 @@
+"""Shared helpers of the GPU parity tests: device copies of a workload and
+the comparison rule against the oracle.
+
+Comparison rule: token ids, accepted lengths and fork tokens bit-exact for
+every sequence the oracle does not flag (a flagged sequence has a uniform
+within 1e-6 of a decision boundary); probabilities within 1e-5 relative
+(|gpu - ref| <= 1e-5 |ref| + 1e-30); residual probabilities within
+1e-5 (p_t + q_t) / Z, since a difference of nearly equal probabilities has
+no meaningful relative error.
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+RTOL = 1e-5
+ATOL = 1e-30
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def dev_inputs(w):
+    return dict(
+        T=to_dev(w.target, w.dtype), D=to_dev(w.draft, w.dtype),
+        d=torch.from_numpy(np.ascontiguousarray(w.draft_tokens)).cuda(),
+        tau=torch.from_numpy(np.ascontiguousarray(w.temperature)).cuda(),
+        ua=torch.from_numpy(np.ascontiguousarray(w.u_accept)).cuda(),
+        ur=torch.from_numpy(np.ascontiguousarray(w.u_recover)).cuda())
+
+
+def assert_probs_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), f"{what}: NaN pattern differs"
+    g, r = got[~nan_ref], ref[~nan_ref]
+    bad = np.abs(g - r) > RTOL * np.abs(r) + ATOL
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside 1e-5 rel: "
+                             f"got {g[i]} ref {r[i]}")
+
+
+def compare_verify(out, ref, seqs, f, k, want_p=True, want_q=True):
+    """Compares the GPU outputs (full batch) at sequences `seqs` with the
+    oracle's BatchResult over the same sequences.  Returns (n_flagged,
+    n_compared)."""
+    al = out["accept_len"].cpu().numpy()[seqs]
+    tok = out["out_token"].cpu().numpy()[seqs]
+    n_flag = 0
+    for i in range(len(seqs)):
+        if ref.error[i]:
+            assert al[i] == -1 and tok[i] == -1, (seqs[i], al[i], tok[i])
+            continue
+        if ref.flagged[i]:
+            n_flag += 1
+            continue
+        assert al[i] == ref.accept_len[i], (int(seqs[i]), int(al[i]), int(ref.accept_len[i]))
+        assert tok[i] == ref.token[i], (int(seqs[i]), int(tok[i]), int(ref.token[i]))
+    if want_p:
+        assert_probs_close(out["p_draft"].cpu().numpy()[seqs], ref.p_draft, "p_draft")
+    if want_q:
+        assert_probs_close(out["q_draft"].cpu().numpy()[seqs], ref.q_draft, "q_draft")
+    if f:
+        ft = out["fork_tokens"].cpu().numpy()[seqs]
+        np.testing.assert_array_equal(ft, ref.fork_tokens, err_msg="fork tokens")
+        assert_probs_close(out["fork_probs"].cpu().numpy()[seqs], ref.fork_probs, "fork probs")
+    return n_flag, len(seqs)
+
+
+def residual_tolerance(T, D, dtype, tau, k):
+    """Per-element tolerance of the normalised residual rows of one
+    sequence: 1e-5 (p + q) / Z for j < k, 1e-5 p at j = k (float64)."""
+    V = T.shape[-1]
+    tol = np.empty((k + 1, V))
+    for j in range(k + 1):
+        P = oracle.softmax_temp(oracle.widen(T[j], dtype), tau)
+        if j < k:
+            Q = oracle.softmax_temp(oracle.widen(D[j], dtype), tau)
+            w = np.maximum(P - Q, 0)
+            Z = w.sum()
+            tol[j] = RTOL * (P + Q) / Z if Z > 0 else RTOL * P
+        else:
+            tol[j] = RTOL * P
+    return tol + ATOL
+
+
+def assert_residual_close(got, ref, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), f"{what}: NaN pattern differs"
+    d = np.abs(got - ref)
+    bad = (d > tol) & ~nan_ref
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} elements outside tolerance: got "
+                             f"{got.ravel()[i]} ref {ref.ravel()[i]} tol {tol.ravel()[i]}")

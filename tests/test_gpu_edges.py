@@ -1,0 +1,235 @@
+"""GPU parity on edge cases: ragged and tiny vocabularies, k = 1 and 63,
+f = 1, 16 and V-1, ties, identical and disjoint drafters, error sequences,
+empty batches, strided inputs, every draw position, softmax rows and the
+standalone fork call."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import (assert_probs_close, assert_residual_close,
+                               compare_verify, log, residual_tolerance, to_dev)
+from workloads import Config, f32_to_bf16_bits, make_workload, uniforms
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from verification_sampling_amd import specverify
+    specverify.lib()
+    return specverify
+
+
+def _pad(n, dtype):
+    m = 8 if dtype == "bf16" else 4
+    return (n + m - 1) // m * m
+
+
+def padded_dev(arr, dtype):
+    """Device copy of [B, K1, V] logits in a row-padded buffer (16-byte
+    aligned rows), returned as a [B, K1, V] view."""
+    B, K1, V = arr.shape
+    Vp = _pad(V, dtype)
+    host = np.zeros((B, K1, Vp), dtype=arr.dtype)
+    host[:, :, :V] = arr
+    return to_dev(host, dtype)[:, :, :V]
+
+
+def run_case(sv, T, D, dtype, drafts, tau, ua, ur, f, want_q=True):
+    x = dict(T=padded_dev(T, dtype), D=padded_dev(D, dtype))
+    out = sv.verify(x["T"], x["D"], torch.from_numpy(drafts).cuda(), torch.from_numpy(tau).cuda(),
+                    torch.from_numpy(ua).cuda(), torch.from_numpy(ur).cuda(), f=f,
+                    want_p=True, want_q=want_q)
+    torch.cuda.synchronize()
+    ref = oracle.verify_batch(T, D, dtype, drafts, tau, ua, ur, f=f, want_q=want_q)
+    nf, n = compare_verify(out, ref, np.arange(T.shape[0]), f, drafts.shape[1], want_q=want_q)
+    return out, ref, nf
+
+
+def synth(B, k, V, dtype, tau, seed, f=0):
+    return make_workload(Config("edge", B=B, k=k, V=V, f=f, dtype=dtype, profile="zipf",
+                                seed=seed, tau=tau, sigma_range=(0.3, 1.2)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [2, 7, 1000, 2049, 4095, 4097, 8200, 20000])
+def test_ragged_vocabularies(sv, dtype, V):
+    for tau in (0.0, 0.8):
+        for f in sorted({0, 1, min(3, V - 1)}):
+            w = synth(3, 3, V, dtype, tau, seed=V * 7 + int(tau * 10) + f, f=f)
+            run_case(sv, w.target, w.draft, dtype, w.draft_tokens, w.temperature,
+                     w.u_accept, w.u_recover, f)
+    log(f"[edges] ragged V={V} {dtype}: ok")
+
+
+def test_k_limits_and_fan_outs(sv):
+    for (k, V, f, dtype) in [(1, 3000, 2, "bf16"), (63, 3000, 3, "bf16"), (63, 1500, 16, "f32"),
+                             (4, 5000, 16, "bf16"), (3, 9, 8, "bf16"), (2, 17, 16, "f32"),
+                             (5, 33, 5, "bf16")]:
+        for tau in (0.0, 1.1):
+            w = synth(2, k, V, dtype, tau, seed=k * 100 + V + f, f=f)
+            run_case(sv, w.target, w.draft, dtype, w.draft_tokens, w.temperature,
+                     w.u_accept, w.u_recover, f)
+    log("[edges] k in {1, 63}, f in {2, 3, 5, 8, 16}: ok")
+
+
+def test_ties_everywhere(sv):
+    B, k, V = 3, 4, 3000
+    T = np.zeros((B, k + 1, V), dtype=np.float32)
+    T[:, :, 100:110] = 1.0  # ten-way tie at the top
+    D = T.copy()
+    D[1] = 0.0              # flat drafter
+    rng = np.random.default_rng(1)
+    drafts = rng.integers(100, 110, (B, k)).astype(np.int32)
+    drafts[0, 0] = 100
+    for tau in (0.0, 0.7):
+        taus = np.full(B, tau, dtype=np.float32)
+        out, ref, nf = run_case(sv, T, D, "f32", drafts, taus, uniforms(rng, (B, k)),
+                                uniforms(rng, (B, k + 1)), 3)
+        if tau == 0.0:
+            # greedy argmax is the lowest tied id
+            assert ref.token[0] in (100, 101)
+    log("[edges] ties: ok")
+
+
+def test_identical_and_disjoint_drafters(sv):
+    w = synth(4, 5, 6000, "bf16", 0.9, seed=5, f=3)
+    out, ref, _ = run_case(sv, w.target, w.target, "bf16", w.draft_tokens, w.temperature,
+                           w.u_accept, w.u_recover, 3)
+    assert np.all(out["accept_len"].cpu().numpy() == 5)
+    B, k, V = 2, 3, 600
+    T = np.full((B, k + 1, V), -np.inf, dtype=np.float32)
+    D = np.full((B, k + 1, V), -np.inf, dtype=np.float32)
+    T[:, :, :300] = 0.5
+    D[:, :, 300:] = 0.25
+    drafts = np.array([[301, 302, 303], [400, 500, 599]], dtype=np.int32)
+    rng = np.random.default_rng(2)
+    out, ref, _ = run_case(sv, T, D, "f32", drafts, np.full(B, 1.0, np.float32),
+                           uniforms(rng, (B, k)), uniforms(rng, (B, k + 1)), 2)
+    assert np.all(out["accept_len"].cpu().numpy() == 0)
+    assert np.all(out["out_token"].cpu().numpy() < 300)
+    log("[edges] identical / disjoint drafters: ok")
+
+
+def test_error_sequences(sv):
+    B, k, V = 6, 3, 2500
+    w = synth(B, k, V, "bf16", 0.8, seed=9, f=2)
+    T, D = w.target.copy(), w.draft.copy()
+    drafts = w.draft_tokens.copy()
+    tau = w.temperature.copy()
+    drafts[0, 1] = V          # drafted id out of range
+    drafts[1, 2] = -3
+    tau[2] = -0.5             # negative temperature
+    tau[3] = np.nan
+    ninf = f32_to_bf16_bits(np.array([-np.inf], dtype=np.float32))[0]
+    pinf = f32_to_bf16_bits(np.array([np.inf], dtype=np.float32))[0]
+    T[4, 2, :] = ninf          # target row with no finite entry
+    D[5, 1, 17] = pinf         # draft row with +inf
+    out, ref, _ = run_case(sv, T, D, "bf16", drafts, tau, w.u_accept, w.u_recover, 2)
+    assert ref.error[:6].all()
+    ft = out["fork_tokens"].cpu().numpy()
+    assert np.all(ft[:6] == -1)
+    assert np.all(np.isnan(out["fork_probs"].cpu().numpy()[:6]))
+    assert np.all(np.isnan(out["p_draft"].cpu().numpy()[:6]))
+    log("[edges] error sequences: ok")
+
+
+def test_empty_batch_and_strided_inputs(sv):
+    w = synth(3, 2, 3000, "bf16", 0.6, seed=11, f=2)
+    e = sv.verify(to_dev(w.target[:0], "bf16"), to_dev(w.draft[:0], "bf16"),
+                  torch.zeros(0, 2, dtype=torch.int32, device="cuda"),
+                  torch.zeros(0, dtype=torch.float32, device="cuda"),
+                  torch.zeros(0, 2, dtype=torch.float32, device="cuda"),
+                  torch.zeros(0, 3, dtype=torch.float32, device="cuda"), f=2)
+    torch.cuda.synchronize()
+    assert e["accept_len"].numel() == 0
+    # a draft batch that lives inside a larger buffer, every other sequence
+    big = np.zeros((6, 3, 3000), dtype=np.uint16)
+    big[::2] = w.draft
+    Dv = to_dev(big, "bf16")[::2]
+    Tv = to_dev(w.target, "bf16")
+    out = sv.verify(Tv, Dv, torch.from_numpy(w.draft_tokens).cuda(),
+                    torch.from_numpy(w.temperature).cuda(), torch.from_numpy(w.u_accept).cuda(),
+                    torch.from_numpy(w.u_recover).cuda(), f=2, want_p=True, want_q=True)
+    torch.cuda.synchronize()
+    ref = oracle.verify_batch(w.target, w.draft, "bf16", w.draft_tokens, w.temperature,
+                              w.u_accept, w.u_recover, f=2)
+    compare_verify(out, ref, np.arange(3), 2, 2)
+    log("[edges] empty batch, strided inputs: ok")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_residual_sample_every_position(sv, dtype):
+    B, k, V = 4, 3, 5000
+    w = synth(B, k, V, dtype, 0.9, seed=13)
+    tau = w.temperature.copy()
+    tau[1] = 0.0
+    x = dict(T=padded_dev(w.target, dtype), D=padded_dev(w.draft, dtype))
+    d = torch.from_numpy(w.draft_tokens).cuda()
+    for pos_v in range(k + 1):
+        pos = np.full(B, pos_v, dtype=np.int32)
+        pos[3] = k + 1 if pos_v == 0 else pos_v   # out of range once
+        out = sv.residual_sample(x["T"], x["D"], d, torch.from_numpy(tau).cuda(),
+                                 torch.from_numpy(pos).cuda(),
+                                 torch.from_numpy(w.u_recover).cuda(), want_residual=True)
+        torch.cuda.synchronize()
+        for b in range(B):
+            tok, flag, res, err = oracle.sample_at_position(
+                w.target[b], w.draft[b], dtype, w.draft_tokens[b], tau[b], pos[b],
+                w.u_recover[b], want_residual=True)
+            g = int(out["token"][b])
+            if err:
+                assert g == -1
+                assert np.all(np.isnan(out["residual"][b].cpu().numpy()))
+                continue
+            if not flag:
+                assert g == tok, (pos_v, b, g, tok)
+            tol = residual_tolerance(w.target[b], w.draft[b], dtype, float(tau[b]), k)
+            assert_residual_close(out["residual"][b].cpu().numpy(), res, tol,
+                                  f"residual b={b} pos={pos_v}")
+        # without the residual output only the drawn row is read
+        out2 = sv.residual_sample(x["T"], x["D"], d, torch.from_numpy(tau).cuda(),
+                                  torch.from_numpy(pos).cuda(),
+                                  torch.from_numpy(w.u_recover).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(out2["token"], out["token"])
+    log(f"[edges] residual_sample every position {dtype}: ok")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_softmax_rows(sv, dtype):
+    rows, V = 12, 7000
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((rows, V)) * 3).astype(np.float32)
+    x[5, :] = -np.inf
+    host = f32_to_bf16_bits(np.where(np.isfinite(x), x, 0)) if dtype == "bf16" else x
+    if dtype == "bf16":
+        host[5, :] = f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
+    tau = np.array([0.7, 0.0, 1.5, -1.0, 0.3, 2.0], dtype=np.float32)  # two rows per temperature
+    dev = padded_dev(host[None], dtype)[0]
+    got = sv.softmax_temp(dev, torch.from_numpy(tau).cuda(), rows_per_temp=2)
+    torch.cuda.synchronize()
+    ref = oracle.softmax_rows(host, dtype, np.repeat(tau, 2))
+    assert_probs_close(got.cpu().numpy(), ref, f"softmax {dtype}")
+    log(f"[edges] softmax rows {dtype}: ok")
+
+
+@pytest.mark.parametrize("f", [1, 3, 16])
+def test_forked_topf_standalone(sv, f):
+    B, k, V = 5, 4, 9000
+    w = synth(B, k, V, "bf16", 0.8, seed=19 + f)
+    tau = w.temperature.copy()
+    tau[2] = 0.0
+    drafts = w.draft_tokens.copy()
+    drafts[4, 0] = V + 5  # error sequence
+    toks, probs = sv.forked_topf(to_dev(w.draft, "bf16"), torch.from_numpy(drafts).cuda(),
+                                 torch.from_numpy(tau).cuda(), f)
+    torch.cuda.synchronize()
+    rt, rp = oracle.forked_topf_batch(w.draft, "bf16", drafts, tau, f)
+    np.testing.assert_array_equal(toks.cpu().numpy(), rt)
+    assert_probs_close(probs.cpu().numpy(), rp, "fork probs")
+    log(f"[edges] forked_topf f={f}: ok")

@@ -1,0 +1,302 @@
+"""Python binding of libspecverify (ctypes).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream; tensors must live on
+a ROCm device.  The library must have been built (``build_lib.py``); nothing
+falls back to the CPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_OK = 0
+SV_F32 = 0
+SV_BF16 = 1
+
+_lib = None
+_lock = threading.Lock()
+
+
+class SvBatch(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("target", ctypes.c_void_p),
+        ("t_seq_stride", ctypes.c_int64), ("t_row_stride", ctypes.c_int64),
+        ("draft", ctypes.c_void_p),
+        ("d_seq_stride", ctypes.c_int64), ("d_row_stride", ctypes.c_int64),
+        ("draft_tokens", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+    ]
+
+
+class SvForks(ctypes.Structure):
+    _fields_ = [("f", ctypes.c_int32), ("tokens", ctypes.c_void_p),
+                ("probs", ctypes.c_void_p)]
+
+
+class SvOpts(ctypes.Structure):
+    _fields_ = [("ev_stats_begin", ctypes.c_void_p),
+                ("ev_stats_end", ctypes.c_void_p)]
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise SpecVerifyError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m verification_sampling_amd.build_lib`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            L.sv_workspace_size.argtypes = [i32, i32, i32, i32]
+            L.sv_workspace_size.restype = sz
+            L.sv_workspace_init.argtypes = [vp, sz, vp]
+            L.sv_workspace_init.restype = i32
+            L.sv_status_string.argtypes = [i32]
+            L.sv_status_string.restype = ctypes.c_char_p
+            L.sv_version.argtypes = []
+            L.sv_version.restype = ctypes.c_char_p
+            L.sv_softmax_temp.argtypes = [vp, i32, i64, i32, i64, vp, i64, vp, i64, vp, sz, vp]
+            L.sv_softmax_temp.restype = i32
+            pb = ctypes.POINTER(SvBatch)
+            pf = ctypes.POINTER(SvForks)
+            po = ctypes.POINTER(SvOpts)
+            L.sv_verify.argtypes = [pb, vp, vp, vp, vp, vp, vp, pf, vp, sz, vp]
+            L.sv_verify.restype = i32
+            L.sv_verify_ex.argtypes = [pb, vp, vp, vp, vp, vp, vp, pf, vp, sz, vp, po]
+            L.sv_verify_ex.restype = i32
+            L.sv_residual_sample.argtypes = [pb, vp, vp, vp, vp, i64, i64, vp, sz, vp]
+            L.sv_residual_sample.restype = i32
+            L.sv_forked_topf.argtypes = [pb, pf, vp, sz, vp]
+            L.sv_forked_topf.restype = i32
+            _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().sv_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != SV_OK:
+        raise SpecVerifyError(f"{what} failed: {status_string(code)}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream_handle(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ workspace
+
+class Workspace:
+    """A zero-filled device buffer for the library's scratch data.  The
+    library leaves it zero-filled in the parts that must start at zero, so
+    one buffer serves any number of calls; calls sharing it must not overlap
+    (one workspace per stream)."""
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8,
+                                   device=self.device)
+        return self.buf
+
+
+_ws_cache = {}
+
+
+def default_workspace(device=None, stream=None) -> Workspace:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    key = (dev.index, s.cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = _ws_cache[key] = Workspace(dev)
+    return ws
+
+
+def workspace_size(B: int, k: int, V: int, f: int = 0) -> int:
+    n = lib().sv_workspace_size(int(B), int(k), int(V), int(f))
+    if n == 0:
+        raise SpecVerifyError("sizes out of range for the workspace")
+    return int(n)
+
+
+# ------------------------------------------------------------------ helpers
+
+def _batch(target, draft, draft_tokens, temperature):
+    ref = draft if target is None else target
+    if ref.dim() != 3 or ref.stride(2) != 1:
+        raise ValueError("logits must be [B, k+1, V] with V contiguous")
+    if draft.stride(2) != 1:
+        raise ValueError("draft logits must have V contiguous")
+    B, K1, V = ref.shape
+    k = draft_tokens.shape[1]
+    if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be contiguous int32 [B, k]")
+    if temperature.dtype != torch.float32 or not temperature.is_contiguous():
+        raise ValueError("temperature must be contiguous float32 [B]")
+    if target is not None and target.dtype != draft.dtype:
+        raise ValueError("target and draft logits must share a dtype")
+    b = SvBatch()
+    b.B, b.k, b.V = int(B), int(k), int(V)
+    b.dtype = _dtype_code(ref)
+    if target is not None:
+        b.target = target.data_ptr()
+        b.t_seq_stride, b.t_row_stride = target.stride(0), target.stride(1)
+    b.draft = draft.data_ptr()
+    b.d_seq_stride, b.d_row_stride = draft.stride(0), draft.stride(1)
+    b.draft_tokens = draft_tokens.data_ptr()
+    b.temperature = temperature.data_ptr()
+    return b
+
+
+def _f32(t, shape, name):
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be contiguous float32 {tuple(shape)}")
+    return t
+
+
+# ------------------------------------------------------------------ API
+
+def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int = 0,
+           want_p: bool = False, want_q: bool = False, workspace: Optional[Workspace] = None,
+           stream=None, out=None, timing_events=None):
+    """sv_verify: returns dict with accept_len [B] int32, out_token [B]
+    int32, and optionally p_draft/q_draft [B,k] float32 and fork_tokens
+    [B,k+1,f] int32 / fork_probs [B,k+1,f] float32."""
+    b = _batch(target, draft, draft_tokens, temperature)
+    B, k = b.B, b.k
+    dev = target.device
+    _f32(u_accept, (B, k), "u_accept")
+    _f32(u_recover, (B, k + 1), "u_recover")
+    if out is None:
+        out = {
+            "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "out_token": torch.empty(B, dtype=torch.int32, device=dev),
+        }
+        if want_p:
+            out["p_draft"] = torch.empty(B, k, dtype=torch.float32, device=dev)
+        if want_q:
+            out["q_draft"] = torch.empty(B, k, dtype=torch.float32, device=dev)
+        if f > 0:
+            out["fork_tokens"] = torch.empty(B, k + 1, f, dtype=torch.int32, device=dev)
+            out["fork_probs"] = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
+    forks = None
+    if f > 0:
+        forks = SvForks(int(f), out["fork_tokens"].data_ptr(), out["fork_probs"].data_ptr())
+    ws = workspace or default_workspace(dev, stream)
+    need = workspace_size(B, k, b.V, f)
+    buf = ws.get(need)
+    opts = None
+    if timing_events is not None:
+        opts = SvOpts(timing_events[0], timing_events[1])
+    code = lib().sv_verify_ex(
+        ctypes.byref(b), _ptr(u_accept), _ptr(u_recover), _ptr(out["accept_len"]),
+        _ptr(out["out_token"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+        ctypes.byref(forks) if forks is not None else None,
+        _ptr(buf), buf.numel(), _stream_handle(stream),
+        ctypes.byref(opts) if opts is not None else None)
+    _check(code, "sv_verify")
+    return out
+
+
+def residual_sample(target, draft, draft_tokens, temperature, position, u_recover,
+                    want_residual: bool = False, workspace: Optional[Workspace] = None,
+                    stream=None):
+    """sv_residual_sample: returns dict with token [B] int32 and optionally
+    residual [B,k+1,V] float32."""
+    b = _batch(target, draft, draft_tokens, temperature)
+    B, k, V = b.B, b.k, b.V
+    dev = target.device
+    if position.dtype != torch.int32 or not position.is_contiguous():
+        raise ValueError("position must be contiguous int32 [B]")
+    _f32(u_recover, (B, k + 1), "u_recover")
+    out = {"token": torch.empty(B, dtype=torch.int32, device=dev)}
+    res = None
+    rs0 = rs1 = 0
+    if want_residual:
+        Vp = (V + 3) // 4 * 4
+        res = torch.empty(B, k + 1, Vp, dtype=torch.float32, device=dev)[:, :, :V]
+        rs0, rs1 = res.stride(0), res.stride(1)
+        out["residual"] = res
+    ws = workspace or default_workspace(dev, stream)
+    buf = ws.get(workspace_size(B, k, V, 0))
+    code = lib().sv_residual_sample(
+        ctypes.byref(b), _ptr(position), _ptr(u_recover), _ptr(out["token"]),
+        ctypes.c_void_p(res.data_ptr()) if res is not None else None, rs0, rs1,
+        _ptr(buf), buf.numel(), _stream_handle(stream))
+    _check(code, "sv_residual_sample")
+    return out
+
+
+def forked_topf(draft, draft_tokens, temperature, f: int,
+                workspace: Optional[Workspace] = None, stream=None):
+    """sv_forked_topf: returns (tokens [B,k+1,f] int32, probs [B,k+1,f]
+    float32)."""
+    b = _batch(None, draft, draft_tokens, temperature)
+    B, k = b.B, b.k
+    dev = draft.device
+    toks = torch.empty(B, k + 1, f, dtype=torch.int32, device=dev)
+    probs = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
+    forks = SvForks(int(f), toks.data_ptr(), probs.data_ptr())
+    ws = workspace or default_workspace(dev, stream)
+    buf = ws.get(workspace_size(B, k, b.V, f))
+    code = lib().sv_forked_topf(ctypes.byref(b), ctypes.byref(forks), _ptr(buf),
+                                buf.numel(), _stream_handle(stream))
+    _check(code, "sv_forked_topf")
+    return toks, probs
+
+
+def softmax_temp(logits, temperature, rows_per_temp: int = 1,
+                 workspace: Optional[Workspace] = None, stream=None):
+    """sv_softmax_temp over the rows of a [rows, V] tensor (V contiguous);
+    returns float32 [rows, V]."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, V] with V contiguous")
+    rows, V = logits.shape
+    if temperature.dtype != torch.float32 or not temperature.is_contiguous():
+        raise ValueError("temperature must be contiguous float32")
+    dev = logits.device
+    Vp = (V + 3) // 4 * 4
+    out = torch.empty(rows, Vp, dtype=torch.float32, device=dev)[:, :V]
+    ws = workspace or default_workspace(dev, stream)
+    buf = ws.get(workspace_size(rows, 0, V, 0))
+    code = lib().sv_softmax_temp(
+        _ptr(logits), _dtype_code(logits), int(rows), int(V), logits.stride(0),
+        _ptr(temperature), int(rows_per_temp), ctypes.c_void_p(out.data_ptr()), out.stride(0),
+        _ptr(buf), buf.numel(), _stream_handle(stream))
+    _check(code, "sv_softmax_temp")
+    return out
