@@ -1,0 +1,218 @@
+"""Throughput of the verify-and-speculate step on one MI355X.
+
+One step = one sv_verify call with fused forked top-f over one batch of the
+batched Qwen3-vocabulary workload: B=64 sequences, k=7 drafted positions
+plus the bonus position, f=3, V=151936, bf16 logits, temperature 0.7
+(seeded synthetic Zipf-profile logits; the drafted tokens are drawn from the
+draft distribution).  Inputs are resident in HBM before timing; three input
+sets rotate so that no step finds its 311 MB of logits in the 256 MB
+last-level cache.
+
+Prints one JSON line: rows/s (512 verified (sequence, position) rows per
+step), the roofline of the streaming statistics kernel (algorithmic bytes
+per launch / its average duration, measured with HIP events on the call's
+stream), and the CPU oracle's rows/s on a bounded sample of the same
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("verified (seq×position) rows/s and % of HBM roofline, "
+          "V=151936 k=7 f=3 B=64")
+WORKLOAD = "batched_verify_fork_qwen"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stats_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "verification_sampling_amd", "csrc", n)
+                  for n in ("specverify.hip", "sv_device.h", "sv_stats.h")]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-seqs", type=int, default=16,
+                    help="sequences of the workload the oracle is timed on")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain device copy of the logits' size (counter calibration)")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls needed for event timing."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                               ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        t = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes(B, k, V, f, elem):
+    """Algorithmic bytes: every input byte read once, every output byte
+    written once."""
+    logits = 2 * B * (k + 1) * V * elem          # target + draft, rows 0..k
+    small_in = B * k * 4 + B * 4 + B * k * 4 + B * (k + 1) * 4   # d, tau, u_acc, u_rec
+    out = B * 4 + B * 4 + 2 * B * (k + 1) * f * 4               # len, token, forks
+    stats_kernel = logits + B * k * 4 + B * 4 + B * k * 4 + B * 4 + 2 * B * (k + 1) * f * 4
+    return logits + small_in + out, stats_kernel
+
+
+def cpu_baseline(w, nseq):
+    import oracle
+
+    seqs = list(range(min(nseq, w.B)))
+    t0 = time.perf_counter()
+    oracle.verify_batch(w.target, w.draft, w.dtype, w.draft_tokens, w.temperature,
+                        w.u_accept, w.u_recover, f=w.f, seqs=seqs)
+    dt = time.perf_counter() - t0
+    rows = len(seqs) * (w.k + 1)
+    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.B} sequences of {WORKLOAD} "
+                      f"({rows} rows), one process, {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
+                                   "--gpus must be 1 (the step has no multi-GPU path)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from verification_sampling_amd import specverify as sv
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[WORKLOAD]
+    w = make_workload(cfg)
+    B, k, V, f = cfg.B, cfg.k, cfg.V, cfg.f
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def bf16(a_):
+        return torch.from_numpy(np.ascontiguousarray(a_).view(np.int16)).view(torch.bfloat16)
+
+    base = dict(T=bf16(w.target).to(dev), D=bf16(w.draft).to(dev),
+                d=torch.from_numpy(w.draft_tokens).to(dev),
+                tau=torch.from_numpy(w.temperature).to(dev),
+                ua=torch.from_numpy(w.u_accept).to(dev),
+                ur=torch.from_numpy(w.u_recover).to(dev))
+    # three input sets (the batch rolled by 0, 21 and 42 sequences)
+    sets = []
+    for r in (0, 21, 42):
+        sets.append({key: torch.roll(v, r, 0).contiguous() for key, v in base.items()})
+    del base
+    ws = sv.Workspace(dev)
+    calls = []
+    for s in sets:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_token": torch.empty(B, dtype=torch.int32, device=dev),
+               "fork_tokens": torch.empty(B, k + 1, f, dtype=torch.int32, device=dev),
+               "fork_probs": torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)}
+        calls.append(sv.PreparedVerify(s["T"], s["D"], s["d"], s["tau"], s["ua"], s["ur"],
+                                       f, out, ws))
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    for i in range(a.warmup):
+        calls[i % 3]()
+    torch.cuda.synchronize()
+
+    ev = [(hip.event(), hip.event()) for _ in range(a.steps)]
+    opts = [sv.SvOpts(e0.value, e1.value) for e0, e1 in ev]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(a.steps):
+        calls[i % 3](opts[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    stats_ms = [hip.elapsed_ms(e0, e1) for e0, e1 in ev]
+
+    ms_per_step = total_ms / a.steps
+    rows = B * (k + 1)
+    total_bytes, stats_bytes = alg_bytes(B, k, V, f, 2)
+    stats_avg_s = float(np.mean(stats_ms)) * 1e-3
+    achieved = stats_bytes / stats_avg_s / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    if a.copy_calib:
+        x = torch.empty(total_bytes // 8, dtype=torch.float32, device=dev).normal_()
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": rows / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": B, "k": k, "f": f, "V": V,
+                   "logits": "bf16", "temperature": 0.7, "rows_per_step": rows,
+                   "input_sets": 3},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "k_stats", "alg_bytes_per_launch": stats_bytes,
+                     "avg_launch_us": stats_avg_s * 1e6},
+        "step_alg_GBs": total_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

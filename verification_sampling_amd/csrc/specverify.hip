@@ -57,6 +57,13 @@ struct RowRec {
 };
 static_assert(sizeof(RowRec) == 72, "RowRec layout");
 
+__device__ __forceinline__ void store_row(RowRec* p, const RowRec& r) {
+  st_dev(&p->tm, r.tm); st_dev(&p->targ, r.targ); st_dev(&p->ts, r.ts);
+  st_dev(&p->dm, r.dm); st_dev(&p->darg, r.darg); st_dev(&p->ds, r.ds);
+  st_dev(&p->pd, r.pd); st_dev(&p->qd, r.qd); st_dev(&p->zr, r.zr); st_dev(&p->zp, r.zp);
+  st_dev(&p->valid, r.valid); st_dev(&p->pad, r.pad);
+}
+
 struct SeqRec {
   int n;        // outcome position
   int status;   // 0 error, 1 finished (greedy), 2 residual draw pending
@@ -69,9 +76,10 @@ struct Ws {
   float* tm; double* ts; int* targ;     // [R * cpr] target chunk partials
   float* dm; double* ds; int* darg;     // [R * cpr] draft chunk partials
   float* dtv; int* dti;                 // [R * cpr * F] draft chunk top-f
+  int* ftok; float* fprob;              // [R * F] a row's forks, staged for the sequence
   RowRec* rows;        // [R]
   SeqRec* seqs;        // [B]
-  double* kr; double* kp;               // [R * cpr] residual chunk sums
+  double* kr; double* kp;               // [R * cpr * kU] residual slab sums
 };
 
 struct Params {
@@ -83,6 +91,8 @@ struct Params {
   const float* u_rec;
   const int32_t* position;
   int32_t B, k, V, f, F, cpr, mode, rows_all, want_q;
+  int32_t nseg;            // k_stats: segments per row (one wave each)
+  int32_t seg_chunks;      // k_stats: chunks per segment
   int64_t nslots;          // row slots of k_stats
   int64_t rows_per_temp;   // softmax
   int32_t* accept_len;
@@ -166,16 +176,16 @@ __device__ __forceinline__ Merged merge_chunks(const float* pm, const double* ps
                                                int64_t base, int cpr, bool greedy, double cd) {
   const int lane = lane_id();
   float m = neg_inf();
-  for (int ch = lane; ch < cpr; ch += kLanes) m = fmaxf(m, pm[base + ch]);
+  for (int ch = lane; ch < cpr; ch += kLanes) m = fmaxf(m, ld_dev(pm + base + ch));
   const float M = wave_max(m);
   double s = 0.0;
   int arg = kEmptyId;
   for (int ch = lane; ch < cpr; ch += kLanes) {
-    const float mc = pm[base + ch];
+    const float mc = ld_dev(pm + base + ch);
     if (greedy) {
-      if (mc == M) arg = min(arg, parg[base + ch]);
+      if (mc == M) arg = min(arg, ld_dev(parg + base + ch));
     } else if (finitef(M) && mc > neg_inf()) {
-      s += ps[base + ch] * exp2(((double)mc - (double)M) * cd);
+      s += ld_dev(ps + base + ch) * exp2(((double)mc - (double)M) * cd);
     }
   }
   Merged r;
@@ -183,19 +193,6 @@ __device__ __forceinline__ Merged merge_chunks(const float* pm, const double* ps
   r.s = wave_sum(s);
   r.arg = wave_min(arg);
   return r;
-}
-
-// Sequence-level bookkeeping after a row merge: the last row of a sequence
-// to finish returns true (with acquire ordering).
-__device__ __forceinline__ bool last_of(unsigned* ctr, unsigned count) {
-  __threadfence();
-  unsigned old = 0;
-  if (lane_id() == 0) old = atomicAdd(ctr, 1u);
-  old = uniform(__shfl(old, 0));
-  if (old != count - 1) return false;
-  __threadfence();
-  if (lane_id() == 0) *ctr = 0u;
-  return true;
 }
 
 // Overwrites the per-sequence outputs of an error sequence.
@@ -244,9 +241,9 @@ __device__ __forceinline__ void finalize_sequence(const Params& P, int b) {
   }
   // rows read are valid
   if (P.mode == kResidual && !P.rows_all) {
-    if (lane == 0 && !P.ws.rows[b].valid) ok = false;
+    if (lane == 0 && !ld_dev(&P.ws.rows[b].valid)) ok = false;
   } else if (lane < K1) {
-    if (!P.ws.rows[(int64_t)b * K1 + lane].valid) ok = false;
+    if (!ld_dev(&P.ws.rows[(int64_t)b * K1 + lane].valid)) ok = false;
   }
   const bool seq_ok = __ballot(!ok) == 0ull;
 
@@ -258,22 +255,27 @@ __device__ __forceinline__ void finalize_sequence(const Params& P, int b) {
   } else if (P.mode == kVerify) {
     bool acc = true;
     if (lane < k) {
-      const RowRec& rr = P.ws.rows[(int64_t)b * K1 + lane];
+      const RowRec* rr = &P.ws.rows[(int64_t)b * K1 + lane];
       if (greedy) {
-        acc = (d == rr.targ);
+        acc = (d == ld_dev(&rr->targ));
       } else {
         // a = min(1, p/q); q = 0: a = 1 if p > 0 else 0.  Accept iff u < a.
-        const double p = rr.pd, q = rr.qd;
+        const double p = ld_dev(&rr->pd), q = ld_dev(&rr->qd);
         const double a = (q == 0.0) ? (p > 0.0 ? 1.0 : 0.0) : fmin(1.0, p / q);
         acc = (double)P.u_acc[(int64_t)b * k + lane] < a;
       }
+    }
+    if (lane < k) {
+      const RowRec* rr = &P.ws.rows[(int64_t)b * K1 + lane];
+      if (P.p_draft) P.p_draft[(int64_t)b * k + lane] = (float)ld_dev(&rr->pd);
+      if (P.q_draft) P.q_draft[(int64_t)b * k + lane] = (float)ld_dev(&rr->qd);
     }
     const unsigned long long rej = __ballot(lane < k && !acc);
     const int n = rej ? (__ffsll((long long)rej) - 1) : k;
     sr.n = n;
     if (greedy) {
       sr.status = 1;
-      if (lane == 0) P.out_token[b] = P.ws.rows[(int64_t)b * K1 + n].targ;
+      if (lane == 0) P.out_token[b] = ld_dev(&P.ws.rows[(int64_t)b * K1 + n].targ);
     } else {
       sr.status = 2;
     }
@@ -283,12 +285,21 @@ __device__ __forceinline__ void finalize_sequence(const Params& P, int b) {
     if (greedy) {
       sr.status = 1;
       const int64_t rs = P.rows_all ? (int64_t)b * K1 + pos : (int64_t)b;
-      if (lane == 0) P.out_token[b] = P.ws.rows[rs].targ;
+      if (lane == 0) P.out_token[b] = ld_dev(&P.ws.rows[rs].targ);
     } else {
       sr.status = 2;
     }
   } else {
     sr.status = 1;
+  }
+  if (seq_ok && P.fork_tok) {
+    // forks staged by the row merges: rows b*(k+1) .. b*(k+1)+k
+    for (int t = lane; t < K1 * P.f; t += kLanes) {
+      const int jj = t / P.f, r = t - jj * P.f;
+      const int64_t src = ((int64_t)b * K1 + jj) * P.F + r;
+      P.fork_tok[(int64_t)b * K1 * P.f + t] = ld_dev(P.ws.ftok + src);
+      if (P.fork_prob) P.fork_prob[(int64_t)b * K1 * P.f + t] = ld_dev(P.ws.fprob + src);
+    }
   }
   if (lane == 0) P.ws.seqs[b] = sr;
 }
@@ -299,8 +310,8 @@ template <typename In, int F>
 __device__ __forceinline__ void row_merge(const Params& P, int64_t slot, int b, int j, float tau,
                           const RowPlan& pl) {
   const int lane = lane_id();
-  const int cpr = P.cpr;
-  const int64_t base = slot * cpr;
+  const int np = P.nseg;               // one partial per segment
+  const int64_t base = slot * P.cpr;   // partial arrays have a stride of cpr per row
   const float c = pl.greedy ? 0.0f : scale_of(tau);
   const double cd = (double)c;
   const Ws& W = P.ws;
@@ -323,7 +334,7 @@ __device__ __forceinline__ void row_merge(const Params& P, int64_t slot, int b, 
   }
 
   if (pl.readT) {
-    const Merged t = merge_chunks(W.tm, W.ts, W.targ, base, cpr, pl.greedy, cd);
+    const Merged t = merge_chunks(W.tm, W.ts, W.targ, base, np, pl.greedy, cd);
     rec.tm = t.m; rec.ts = t.s; rec.targ = t.arg;
     valid = valid && finitef(t.m);
   }
@@ -335,35 +346,30 @@ __device__ __forceinline__ void row_merge(const Params& P, int64_t slot, int b, 
   }
 
   if (pl.readD) {
-    const Merged q = merge_chunks(W.dm, W.ds, W.darg, base, cpr, pl.greedy, cd);
+    const Merged q = merge_chunks(W.dm, W.ds, W.darg, base, np, pl.greedy, cd);
     if (pl.topf) {
       // Fork candidates: merge the chunks' lists, keep the top f.
       TopList<F> mine;
       mine.clear();
-      for (int ch = lane; ch < cpr; ch += kLanes) {
+      for (int ch = lane; ch < np; ch += kLanes) {
 #pragma unroll
-        for (int r = 0; r < F; ++r) {
-          if (r < P.f) {
-            mine.insert(W.dtv[(base + ch) * F + r], W.dti[(base + ch) * F + r]);
-          }
-        }
+        for (int r = 0; r < F; ++r)
+          mine.insert(ld_dev(W.dtv + (base + ch) * F + r), ld_dev(W.dti + (base + ch) * F + r));
       }
       TopList<F> top;
       wave_merge_lists<F>(mine, P.f, top);
       // Masked softmax at tau of the selected tokens: 2^((v - m') c) / S'.
-      if (P.fork_tok && lane == 0) {
-        const int64_t o = ((int64_t)b * K1 + j) * P.f;
+      // Staged in the workspace; the sequence's last wave writes the outputs.
+      if (lane == 0) {
 #pragma unroll
         for (int r = 0; r < F; ++r) {
           if (r < P.f) {
-            P.fork_tok[o + r] = top.i[r];
-            if (P.fork_prob) {
-              float pr;
-              if (pl.greedy) pr = (r == 0) ? 1.0f : 0.0f;
-              else if (!finitef(q.m) || !(top.v[r] > neg_inf())) pr = 0.0f;
-              else pr = (float)(exp2(((double)top.v[r] - (double)q.m) * cd) / q.s);
-              P.fork_prob[o + r] = pr;
-            }
+            float pr;
+            if (pl.greedy) pr = (r == 0) ? 1.0f : 0.0f;
+            else if (!finitef(q.m) || !(top.v[r] > neg_inf())) pr = 0.0f;
+            else pr = (float)(exp2(((double)top.v[r] - (double)q.m) * cd) / q.s);
+            st_dev(W.ftok + slot * F + r, top.i[r]);
+            st_dev(W.fprob + slot * F + r, pr);
           }
         }
       }
@@ -401,28 +407,149 @@ __device__ __forceinline__ void row_merge(const Params& P, int64_t slot, int b, 
         rec.pd = exp2(((double)xd - (double)rec.tm) * cd) / rec.ts;
         rec.qd = exp2(((double)yd - (double)rec.dm) * cd) / rec.ds;
       }
-      if (lane == 0) {
-        if (P.p_draft) P.p_draft[(int64_t)b * k + j] = (float)rec.pd;
-        if (P.q_draft) P.q_draft[(int64_t)b * k + j] = (float)rec.qd;
-      }
     }
   }
   rec.valid = valid ? 1 : 0;
-  if (lane == 0) W.rows[slot] = rec;
+  if (lane == 0) store_row(&W.rows[slot], rec);
 
   if (P.mode == kSoftmax) return;
   const unsigned rows_per_seq = (P.mode == kResidual && !P.rows_all) ? 1u : (unsigned)K1;
-  if (!last_of(&W.seq_ctr[b], rows_per_seq)) return;
+  if (!arrive_last(&W.seq_ctr[b], rows_per_seq)) return;
   finalize_sequence(P, b);
 }
 
+// The drafted token leaves the draft row's masked statistics: the element
+// is set to -inf in the lane that holds it (rare: one chunk per row).
+template <typename In>
+struct Vec4 {
+  uint4 v[kU];
+};
+
+template <typename In>
+__device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 v3, int64_t cstart,
+                                            int64_t mask_id) {
+  constexpr int VEC = Elem<In>::VEC;
+  static_assert(kU == 4, "mask_token takes four vectors");
+  Vec4<In> r;
+  r.v[0] = v0; r.v[1] = v1; r.v[2] = v2; r.v[3] = v3;
+  const int lane = lane_id();
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (cstart + (int64_t)(u * kLanes + lane) * VEC + e == mask_id) set_neg_inf<In>(r.v[u], e);
+    }
+  }
+  return r;
+}
+
+// Fork-candidate state of one wave (the buffer lives in LDS).
+struct WaveCand {
+  float* cv;
+  int* ci;
+  CandState st;
+};
+
+// One chunk of one row segment, already in registers.  RT / RD: the target
+// / draft row is read; GREEDY: temperature 0.
+template <typename In, int F, bool RT, bool RD, bool GREEDY>
+__device__ __forceinline__ void stats_chunk(const Params& P, const RowPlan& pl, uint4 (&traw)[kU],
+                                            uint4 (&draw)[kU], int ch, bool first, float c,
+                                            LaneStats& ta, LaneStats& da, WaveCand& wc) {
+  constexpr int CH = chunk_elems<In>();
+  const int64_t cstart = (int64_t)ch * CH;
+  if constexpr (RT) {
+    if constexpr (GREEDY) {
+      float m8[kU], mc;
+      fold_greedy<In>(ta, traw, cstart, true, m8, mc);
+    } else {
+      float vs[kU], lm;
+      fold_warm<In>(ta, traw, c, first, vs, lm);
+    }
+  }
+  if constexpr (RD) {
+    if (pl.mask_id >= cstart && pl.mask_id < cstart + CH) {
+      const Vec4<In> m = mask_token<In>(draw[0], draw[1], draw[2], draw[3], cstart, pl.mask_id);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) draw[u] = m.v[u];
+    }
+    unsigned candbits = 0;
+    if constexpr (GREEDY) {
+      float m8[kU], mc;
+      fold_greedy<In>(da, draw, cstart, !pl.topf, m8, mc);
+      if constexpr (F > 0) {
+        if (pl.topf) {
+          if (first) wc.st.kv = wave_fth_largest<F>(mc, F);
+#pragma unroll
+          for (int u = 0; u < kU; ++u) candbits |= (m8[u] >= wc.st.kv) ? (1u << u) : 0u;
+        }
+      }
+    } else {
+      float vs[kU], lm;
+      fold_warm<In>(da, draw, c, first, vs, lm);
+      if constexpr (F > 0) {
+        if (pl.topf) {
+          if (first) {
+            // every element of the chunk's top-F reaches the F-th largest lane
+            // maximum; the first chunk's candidates are all its vectors there
+            wc.st.kv = wave_fth_largest<F>(lm, F);
+            candbits = 0xFu;
+          } else {
+            // an element at or above kv has a term 2^(x c - hi) of at least
+            // 2^(kv c - hi); a vector whose sum of terms is below that (less a
+            // margin for rounding) has no such element
+            const float eth = __builtin_amdgcn_exp2f(fmaf(wc.st.kv, c, -da.hi)) * 0.999999f;
+#pragma unroll
+            for (int u = 0; u < kU; ++u) candbits |= (vs[u] >= eth) ? (1u << u) : 0u;
+          }
+        }
+      }
+    }
+    if constexpr (F > 0) {
+      if (pl.topf) {
+        if (__ballot(candbits != 0u))
+          wc.st = cand_chunk<In, F>(draw[0], draw[1], draw[2], draw[3], candbits, cstart, P.V,
+                                    pl.mask_id, wc.cv, wc.ci, wc.st);
+        if (first) wc.st = cand_compact<F>(wc.cv, wc.ci, wc.st);
+      }
+    }
+  }
+}
+
+// A row segment [c0, c1): full chunks [c0, cfull), then at most one partial
+// chunk.  Target and draft loads of a chunk are issued together.
+template <typename In, int F, bool RT, bool RD, bool GREEDY>
+__device__ __forceinline__ void stats_segment(const Params& P, const RowPlan& pl, const In* trow,
+                                              const In* drow, int c0, int c1, int cfull, float c,
+                                              LaneStats& ta, LaneStats& da, WaveCand& wc) {
+  constexpr int CH = chunk_elems<In>();
+  for (int ch = c0; ch < c1; ++ch) {
+    const bool full = ch < cfull;
+    uint4 t[kU], d[kU];
+    if constexpr (RT) load_chunk<In>(trow, (int64_t)ch * CH, P.V, full, t);
+    if constexpr (RD) load_chunk<In>(drow, (int64_t)ch * CH, P.V, full, d);
+    stats_chunk<In, F, RT, RD, GREEDY>(P, pl, t, d, ch, ch == c0, c, ta, da, wc);
+  }
+}
+
+// Occupancy target of the statistics kernel (waves per SIMD); 0 leaves the
+// register budget to the compiler.
+#ifndef SV_STATS_WAVES_PER_EU
+#define SV_STATS_WAVES_PER_EU 0
+#endif
+#if SV_STATS_WAVES_PER_EU > 0
+#define SV_STATS_ATTR __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU, 8)))
+#else
+#define SV_STATS_ATTR
+#endif
+
 template <typename In, int F>
-__global__ __launch_bounds__(kBlock) void k_stats(Params P) {
+__global__ __launch_bounds__(kBlock) SV_STATS_ATTR void k_stats(Params P) {
   constexpr int CH = chunk_elems<In>();
   const int64_t task = wave_global_id();
-  if (task >= P.nslots * P.cpr) return;
-  const int64_t slot = task / P.cpr;
-  const int chunk = (int)(task - slot * P.cpr);
+  if (task >= P.nslots * P.nseg) return;
+  const int64_t slot = task / P.nseg;
+  const int seg = (int)(task - slot * P.nseg);
   int b, j;
   slot_to_bj(P, slot, b, j);
   b = uniform(b);
@@ -430,38 +557,69 @@ __global__ __launch_bounds__(kBlock) void k_stats(Params P) {
   const float tau = uniform(slot_tau(P, slot, b));
   const RowPlan pl = plan_row(P, b, j, tau);
   const float c = pl.greedy ? 0.0f : scale_of(tau);
-  const int64_t cstart = (int64_t)chunk * CH;
-  const bool full = cstart + CH <= P.V;
   const int lane = lane_id();
   const Ws& W = P.ws;
+  const int c0 = seg * P.seg_chunks;
+  const int c1 = min(c0 + P.seg_chunks, P.cpr);
+  const int cfull = min(c1, max(c0, P.V / CH));  // chunks [c0, cfull) lie inside the row
+  const In* trow = pl.readT ? trow_ptr<In>(P, b, j) : nullptr;
+  const In* drow = pl.readD ? drow_ptr<In>(P, b, j) : nullptr;
 
-  uint4 traw[kU], draw[kU];
-  if (pl.readT) load_chunk<In>(trow_ptr<In>(P, b, j), cstart, P.V, full, traw);
-  if (pl.readD) load_chunk<In>(drow_ptr<In>(P, b, j), cstart, P.V, full, draw);
+  LaneStats ta, da;
+  lane_init(ta);
+  lane_init(da);
+  __shared__ float s_cv[kWavesPerBlock * kCandCap];
+  __shared__ int s_ci[kWavesPerBlock * kCandCap];
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WaveCand cb;
+  cb.cv = s_cv + wib * kCandCap;
+  cb.ci = s_ci + wib * kCandCap;
+  cb.st.n = 0;
+  cb.st.kv = neg_inf();
+  // specialised loops: which rows are read and whether the row is greedy
+  if (pl.readT && pl.readD) {
+    if (pl.greedy) stats_segment<In, F, true, true, true>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
+    else stats_segment<In, F, true, true, false>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
+  } else if (pl.readT) {
+    if (pl.greedy) stats_segment<In, F, true, false, true>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
+    else stats_segment<In, F, true, false, false>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
+  } else if (pl.readD) {
+    if (pl.greedy) stats_segment<In, F, false, true, true>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
+    else stats_segment<In, F, false, true, false>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
+  }
+  TopList<F> wl;
+  wl.clear();
+  if constexpr (F > 0) {
+    if (pl.topf) {
+      CandBuf buf;
+      buf.v = cb.cv;
+      buf.id = cb.ci;
+      buf.n = cb.st.n;
+      buf.kv = cb.st.kv;
+      cand_select<F>(buf, wl);
+    }
+  }
 
+  const int64_t part = slot * P.cpr + seg;
   if (pl.readT) {
-    const ChunkStats<0> s = chunk_stats<In, 0>(traw, cstart, P.V, c, pl.greedy, -1, pl.greedy, 0);
-    if (lane == 0) { W.tm[task] = s.m; W.ts[task] = s.s; W.targ[task] = s.arg; }
+    const WaveStats w = wave_finish(ta, c, pl.greedy);
+    if (lane == 0) { st_dev(W.tm + part, w.m); st_dev(W.ts + part, w.s); st_dev(W.targ + part, w.arg); }
   }
   if (pl.readD) {
-    if constexpr (F > 0) {
-      if (pl.topf) {
-        const ChunkStats<F> s = chunk_stats<In, F>(draw, cstart, P.V, c, pl.greedy, pl.mask_id,
-                                                   false, P.f);
-        if (lane == 0) {
-          W.dm[task] = s.m; W.ds[task] = s.s; W.darg[task] = kEmptyId;
+    const WaveStats w = wave_finish(da, c, pl.greedy);
+    if (lane == 0) {
+      st_dev(W.dm + part, w.m); st_dev(W.ds + part, w.s); st_dev(W.darg + part, w.arg);
+      if constexpr (F > 0) {
 #pragma unroll
-          for (int r = 0; r < F; ++r) { W.dtv[task * F + r] = s.top.v[r]; W.dti[task * F + r] = s.top.i[r]; }
+        for (int r = 0; r < F; ++r) {
+          st_dev(W.dtv + part * F + r, wl.v[r]);
+          st_dev(W.dti + part * F + r, wl.i[r]);
         }
       }
     }
-    if (!pl.topf) {
-      const ChunkStats<0> s = chunk_stats<In, 0>(draw, cstart, P.V, c, pl.greedy, -1, pl.greedy, 0);
-      if (lane == 0) { W.dm[task] = s.m; W.ds[task] = s.s; W.darg[task] = s.arg; }
-    }
   }
 
-  if (!last_of(&W.row_ctr[slot], (unsigned)P.cpr)) return;
+  if (!arrive_last(&W.row_ctr[slot], (unsigned)P.nseg)) return;
   row_merge<In, F>(P, slot, b, j, tau, pl);
 }
 
@@ -525,23 +683,6 @@ __device__ __forceinline__ float vec_sum(const float (&w)[N]) {
   return a[0];
 }
 
-// Lane sums of r and p over one chunk: fp32 pairwise inside each vector,
-// fp64 across the lane's vectors in element order.
-template <typename In>
-__device__ __forceinline__ void resid_lane_sums(const ResidCoef& kc, const uint4 (&traw)[kU],
-                                                const uint4 (&draw)[kU], double& sr, double& sp) {
-  constexpr int VEC = Elem<In>::VEC;
-  sr = 0.0;
-  sp = 0.0;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    float r[VEC], p[VEC];
-    resid_vec<In>(kc, traw[u], draw[u], r, p);
-    sr += (double)vec_sum<VEC>(r);
-    sp += (double)vec_sum<VEC>(p);
-  }
-}
-
 // k_resid slot -> (b, j, record slot).
 __device__ __forceinline__ void resid_slot(const Params& P, int64_t slot, int& b, int& j,
                                            int64_t& rslot, bool& draw_row) {
@@ -559,103 +700,128 @@ __device__ __forceinline__ void resid_slot(const Params& P, int64_t slot, int& b
   }
 }
 
+// The draw of one row, by the wave that finished its residual sums.  Token
+// order inside a chunk is slab by slab: slab u holds vector u of lanes
+// 0..63, i.e. 64 consecutive 16-byte vectors.  The chunk holding the target
+// is found from the chunk sums, the slab from that chunk's slab sums, the
+// lane from a scan of one re-read slab, and the token inside the lane's
+// vector.  Every step keeps to tokens of positive weight: the token is the
+// first one whose running total passes u*Z, or the last positive one if
+// rounding leaves none.
 template <typename In>
-__device__ __forceinline__ void resid_draw(const Params& P, int64_t slot, int b, int j, const RowRec& rr,
-                           const ResidCoef& kc, double Zr, double Zp) {
+__device__ __forceinline__ void resid_draw(const Params& P, int64_t slot, int b, int j,
+                                           const ResidCoef& kc, double Zr, double Zp) {
   constexpr int VEC = Elem<In>::VEC;
   constexpr int CH = chunk_elems<In>();
   const int lane = lane_id();
   const int cpr = P.cpr;
-  const int64_t base = slot * cpr;
   const bool use_r = (j < P.k) && Zr > 0.0;
   const double Z = use_r ? Zr : Zp;
-  const double* sums = use_r ? P.ws.kr : P.ws.kp;
+  const double* slabs = use_r ? P.ws.kr : P.ws.kp;
   const double target = (double)P.u_rec[(int64_t)b * (P.k + 1) + j] * Z;
+  const int64_t sbase = slot * (int64_t)cpr * kU;
 
-  // Chunk holding the target: first chunk whose inclusive prefix exceeds it.
+  // 1. chunk: first whose inclusive prefix passes the target
   int cstar = -1, clast = -1;
   double before = 0.0, before_last = 0.0, carry = 0.0;
+  double sl[kU], sl_last[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) { sl[u] = 0.0; sl_last[u] = 0.0; }
   for (int g = 0; g < cpr; g += kLanes) {
     const int ch = g + lane;
-    const double w = ch < cpr ? sums[base + ch] : 0.0;
+    double v[kU];
+    double w = 0.0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      v[u] = ch < cpr ? ld_dev(slabs + sbase + (int64_t)ch * kU + u) : 0.0;
+      w += v[u];
+    }
     const double incl = carry + wave_inclusive_scan(w);
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = carry;
-    const unsigned long long hit = __ballot(ch < cpr && incl > target);
+    const unsigned long long hit = __ballot(ch < cpr && w > 0.0 && incl > target);
     if (cstar < 0 && hit) {
       const int l = __ffsll((long long)hit) - 1;
       cstar = g + l;
-      before = __shfl(excl, l);
+      before = readlane_d(excl, l);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) sl[u] = readlane_d(v[u], l);
     }
     const unsigned long long posm = __ballot(ch < cpr && w > 0.0);
     if (posm) {
       const int l = 63 - __clzll((long long)posm);
       clast = g + l;
-      before_last = __shfl(excl, l);
+      before_last = readlane_d(excl, l);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) sl_last[u] = readlane_d(v[u], l);
     }
-    carry = __shfl(incl, kLanes - 1);
+    carry = readlane_d(incl, kLanes - 1);
   }
-  if (cstar < 0) { cstar = clast; before = before_last; }
+  if (cstar < 0) {
+    cstar = clast;
+    before = before_last;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) sl[u] = sl_last[u];
+  }
   if (cstar < 0) { cstar = 0; before = 0.0; }
-  cstar = uniform(cstar);
 
-  // Re-read that chunk and locate the token inside it.  Token order inside
-  // a chunk is slab by slab: slab u holds vector u of lanes 0..63, which
-  // are 64 consecutive vectors; a lane's own vectors are 512 elements apart.
-  const int64_t cstart = (int64_t)cstar * CH;
-  const bool full = cstart + CH <= P.V;
-  uint4 traw[kU], draw[kU];
-  load_chunk<In>(trow_ptr<In>(P, b, j), cstart, P.V, full, traw);
-  if (kc.has_q) load_chunk<In>(drow_ptr<In>(P, b, j), cstart, P.V, full, draw);
-
-  double run = before;   // weight of every token before the current slab
-  int tok = -1;
-  int lastpos = -1;      // this lane's last positive-weight token so far
+  // 2. slab inside that chunk (uniform)
+  int ustar = -1, ulast = 0;
+  double ubefore = before, ubefore_last = before, run = before;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    if (tok < 0) {
-      float r[VEC], p[VEC], w[VEC];
-      resid_vec<In>(kc, traw[u], draw[u], r, p);
+    if (sl[u] > 0.0) {
+      if (ustar < 0 && run + sl[u] > target) { ustar = u; ubefore = run; }
+      ulast = u;
+      ubefore_last = run;
+    }
+    run += sl[u];
+  }
+  if (ustar < 0) { ustar = ulast; ubefore = ubefore_last; }
+
+  // 3. re-read that slab (one vector per lane) and find the lane
+  const int64_t cstart = (int64_t)cstar * CH;
+  const int64_t e0 = cstart + (int64_t)(ustar * kLanes + lane) * VEC;
+  float w[VEC];
+  {
+    uint4 tv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
+    const In* tr = trow_ptr<In>(P, b, j);
+    const In* dr = kc.has_q ? drow_ptr<In>(P, b, j) : nullptr;
+    load_vec<In>(tr, e0, P.V, tv);
+    if (kc.has_q) load_vec<In>(dr, e0, P.V, dv);
+    float r[VEC], p[VEC];
+    resid_vec<In>(kc, tv, dv, r, p);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) w[e] = use_r ? r[e] : p[e];
-      const int64_t e0 = cstart + (int64_t)(u * kLanes + lane) * VEC;
+    for (int e = 0; e < VEC; ++e) w[e] = (e0 + e < P.V) ? (use_r ? r[e] : p[e]) : 0.0f;
+  }
+  const float vt = vec_sum<VEC>(w);
+  const double incl = ubefore + wave_inclusive_scan((double)vt);
+  double excl = __shfl_up(incl, 1);
+  if (lane == 0) excl = ubefore;
+  const unsigned long long hit = __ballot(vt > 0.0f && incl > target);
+  const unsigned long long posm = __ballot(vt > 0.0f);
+  const int lstar = hit ? (__ffsll((long long)hit) - 1) : (posm ? 63 - __clzll((long long)posm) : 0);
+
+  // 4. the token inside lane lstar's vector
+  int t = -1, vlast = -1;
+  float acc = 0.0f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        if (w[e] > 0.0f && e0 + e < P.V) lastpos = (int)(e0 + e);
-      const float vt = vec_sum<VEC>(w);
-      const double incl = run + wave_inclusive_scan((double)vt);
-      double excl = __shfl_up(incl, 1);
-      if (lane == 0) excl = run;
-      const unsigned long long hit = __ballot(vt > 0.0f && incl > target);
-      if (hit) {
-        const int l = __ffsll((long long)hit) - 1;
-        int t = -1;
-        if (lane == l) {
-          // first element whose prefix inside the vector passes the target
-          float acc = 0.0f;
-          int vlast = -1;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            acc += w[e];
-            if (w[e] > 0.0f && e0 + e < P.V) {
-              vlast = (int)(e0 + e);
-              if (t < 0 && excl + (double)acc > target) t = (int)(e0 + e);
-            }
-          }
-          if (t < 0) t = vlast;
-        }
-        tok = uniform(__shfl(t, l));
-      }
-      run = __shfl(incl, kLanes - 1);
+  for (int e = 0; e < VEC; ++e) {
+    acc += w[e];
+    if (w[e] > 0.0f) {
+      vlast = (int)(e0 + e);
+      if (t < 0 && excl + (double)acc > target) t = (int)(e0 + e);
     }
   }
-  if (tok < 0) tok = uniform(__shfl(wave_max_int(lastpos), 0));
+  if (t < 0) t = vlast;
+  const int tok = readlane_i(t, lstar);
   if (lane == 0) P.out_token[b] = tok;
 }
 
 template <typename In>
 __global__ __launch_bounds__(kBlock) void k_resid(Params P) {
   constexpr int CH = chunk_elems<In>();
+  constexpr int VEC = Elem<In>::VEC;
   const int64_t task = wave_global_id();
   const int64_t nslots = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
   if (task >= nslots * P.cpr) return;
@@ -679,31 +845,43 @@ __global__ __launch_bounds__(kBlock) void k_resid(Params P) {
   uint4 traw[kU], draw[kU];
   load_chunk<In>(trow_ptr<In>(P, b, j), cstart, P.V, full, traw);
   if (has_q) load_chunk<In>(drow_ptr<In>(P, b, j), cstart, P.V, full, draw);
-  double sr, sp;
-  resid_lane_sums<In>(kc, traw, draw, sr, sp);
-  const double SR = wave_sum(sr);
-  const double SP = wave_sum(sp);
-  if (lane_id() == 0) {
-    P.ws.kr[task] = SR;
-    P.ws.kp[task] = SP;
+  // slab sums of r and p (padding reads -inf: weight 0)
+  const int64_t sbase = (slot * (int64_t)P.cpr + chunk) * kU;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    float r[VEC], p[VEC];
+    resid_vec<In>(kc, traw[u], draw[u], r, p);
+    const double sr = wave_sum((double)vec_sum<VEC>(r));
+    const double sp = wave_sum((double)vec_sum<VEC>(p));
+    if (lane_id() == 0) {
+      st_dev(P.ws.kr + sbase + u, sr);
+      st_dev(P.ws.kp + sbase + u, sp);
+    }
   }
-  if (!last_of(&P.ws.k2_ctr[slot], (unsigned)P.cpr)) return;
+  if (!arrive_last(&P.ws.k2_ctr[slot], (unsigned)P.cpr)) return;
 
   // Row totals, in chunk order.
   const int lane = lane_id();
   double carry_r = 0.0, carry_p = 0.0;
+  const int64_t rbase = slot * (int64_t)P.cpr * kU;
   for (int g = 0; g < P.cpr; g += kLanes) {
     const int ch = g + lane;
-    const double wr = ch < P.cpr ? P.ws.kr[slot * P.cpr + ch] : 0.0;
-    const double wp = ch < P.cpr ? P.ws.kp[slot * P.cpr + ch] : 0.0;
-    carry_r = __shfl(carry_r + wave_inclusive_scan(wr), kLanes - 1);
-    carry_p = __shfl(carry_p + wave_inclusive_scan(wp), kLanes - 1);
+    double wr = 0.0, wp = 0.0;
+    if (ch < P.cpr) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        wr += ld_dev(P.ws.kr + rbase + (int64_t)ch * kU + u);
+        wp += ld_dev(P.ws.kp + rbase + (int64_t)ch * kU + u);
+      }
+    }
+    carry_r = readlane_d(carry_r + wave_inclusive_scan(wr), kLanes - 1);
+    carry_p = readlane_d(carry_p + wave_inclusive_scan(wp), kLanes - 1);
   }
   if (lane == 0) {
     P.ws.rows[rslot].zr = carry_r;
     P.ws.rows[rslot].zp = carry_p;
   }
-  if (draw_row) resid_draw<In>(P, slot, b, j, rr, kc, carry_r, carry_p);
+  if (draw_row) resid_draw<In>(P, slot, b, j, kc, carry_r, carry_p);
 }
 
 // ------------------------------------------------------------ k_write
@@ -802,16 +980,17 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) 
 // ------------------------------------------------------------ host side
 
 struct Layout {
-  size_t row_ctr, seq_ctr, k2_ctr, tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, kr, kp, total;
+  size_t row_ctr, seq_ctr, k2_ctr, tm, ts, targ, dm, ds, darg, dtv, dti, ftok, fprob, rows, seqs,
+      kr, kp, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Candidate-list length of the statistics kernel for fan-out f: 4 covers
+// f <= 4, 16 covers the rest (the top-F contain the top-f).
 static int fork_F(int f) {
   if (f <= 0) return 0;
-  int F = 1;
-  while (F < f) F <<= 1;
-  return F;
+  return f <= 4 ? 4 : 16;
 }
 
 // Workspace layout for R row slots, B sequences, cpr chunks per row and top
@@ -833,10 +1012,12 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   L.darg = take(sizeof(int) * RC);
   L.dtv = take(sizeof(float) * RC * Fa);
   L.dti = take(sizeof(int) * RC * Fa);
+  L.ftok = take(sizeof(int) * R * Fa);
+  L.fprob = take(sizeof(float) * R * Fa);
   L.rows = take(sizeof(RowRec) * R);
   L.seqs = take(sizeof(SeqRec) * B);
-  L.kr = take(sizeof(double) * RC);
-  L.kp = take(sizeof(double) * RC);
+  L.kr = take(sizeof(double) * RC * kU);
+  L.kp = take(sizeof(double) * RC * kU);
   L.total = o;
   return L;
 }
@@ -855,6 +1036,8 @@ static Ws bind_ws(void* base, const Layout& L) {
   w.darg = reinterpret_cast<int*>(p + L.darg);
   w.dtv = reinterpret_cast<float*>(p + L.dtv);
   w.dti = reinterpret_cast<int*>(p + L.dti);
+  w.ftok = reinterpret_cast<int*>(p + L.ftok);
+  w.fprob = reinterpret_cast<float*>(p + L.fprob);
   w.rows = reinterpret_cast<RowRec*>(p + L.rows);
   w.seqs = reinterpret_cast<SeqRec*>(p + L.seqs);
   w.kr = reinterpret_cast<double*>(p + L.kr);
@@ -917,13 +1100,33 @@ static Params base_params(const sv_batch* in) {
   return P;
 }
 
+// Segments: each k_stats wave folds seg_chunks consecutive chunks of one row.
+// The segment size is chosen so that the grid is about one resident round
+// of waves (CUs x 24: six waves per SIMD at the kernel's register use);
+// more chunks per wave amortise the per-wave cross-lane work.
+static void plan_segments(Params& P) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+  }
+  const int64_t target = (int64_t)cus * 24;
+  const int64_t chunks = P.nslots * (int64_t)P.cpr;
+  int64_t g = (chunks + target - 1) / target;
+  if (g < 1) g = 1;
+  if (g > P.cpr) g = P.cpr;
+  P.seg_chunks = (int32_t)g;
+  P.nseg = (int32_t)((P.cpr + g - 1) / g);
+}
+
 static dim3 grid_for(int64_t waves) {
   return dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
 }
 
 template <typename In, int F>
 static hipError_t launch_stats_F(const Params& P, hipStream_t s) {
-  const int64_t waves = P.nslots * P.cpr;
+  const int64_t waves = P.nslots * P.nseg;
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL((k_stats<In, F>), grid_for(waves), dim3(kBlock), 0, s, P);
   return hipGetLastError();
@@ -933,10 +1136,7 @@ template <typename In>
 static hipError_t launch_stats(const Params& P, hipStream_t s) {
   switch (P.F) {
     case 0: return launch_stats_F<In, 0>(P, s);
-    case 1: return launch_stats_F<In, 1>(P, s);
-    case 2: return launch_stats_F<In, 2>(P, s);
     case 4: return launch_stats_F<In, 4>(P, s);
-    case 8: return launch_stats_F<In, 8>(P, s);
     default: return launch_stats_F<In, 16>(P, s);
   }
 }
@@ -959,7 +1159,9 @@ static hipError_t launch_write(const Params& P, hipStream_t s) {
   return hipGetLastError();
 }
 
-static hipError_t dispatch_stats(int dtype, const Params& P, hipStream_t s) {
+static hipError_t dispatch_stats(int dtype, const Params& P0, hipStream_t s) {
+  Params P = P0;
+  plan_segments(P);
   return dtype == SV_BF16 ? launch_stats<uint16_t>(P, s) : launch_stats<float>(P, s);
 }
 static hipError_t dispatch_resid(int dtype, const Params& P, hipStream_t s) {

@@ -16,7 +16,7 @@ namespace sv {
 constexpr int kLanes = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kLanes * kWavesPerBlock;
-constexpr int kU = 8;          // 16-byte vectors per lane per tensor per chunk
+constexpr int kU = 4;          // 16-byte vectors per lane per tensor per chunk
 constexpr int kMaxF = 16;      // largest fork fan-out
 constexpr int kMaxK = 63;      // drafted positions: one lane each in a ballot
 constexpr int kEmptyId = 0x7fffffff;
@@ -41,6 +41,47 @@ __device__ __forceinline__ unsigned uniform(unsigned x) {
 }
 __device__ __forceinline__ float uniform(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// ---------------------------------------------------------------- handoffs
+// Hand-off of data between wavefronts of one launch (a chunk's partials to
+// the wave that merges its row; a row's record to the wave that decides the
+// sequence).  The data are written with device-scope stores (sc1: written
+// through to the device-coherent level) and read with device-scope loads;
+// the writer waits for its stores to complete (s_waitcnt vmcnt(0)) before it
+// bumps the counter with a device-scope atomic, and the reader loads only
+// after seeing the final count.  A device-scope fence would also write back
+// the whole L2 of the wave's XCD, once per wave; this avoids that.
+
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until this wave's vector memory operations have completed.
+__device__ __forceinline__ void vm_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt not waited on
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Publishes this wave's device-scope stores and counts its arrival; returns
+// true on the wave that arrives last (count arrivals in total), which also
+// resets the counter for the next launch.
+__device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned count) {
+  vm_complete();
+  unsigned old = 0;
+  if ((threadIdx.x & 63) == 0)
+    old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = (unsigned)__builtin_amdgcn_readfirstlane((int)__shfl((int)old, 0));
+  if (old != count - 1) return false;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if ((threadIdx.x & 63) == 0) st_dev(ctr, 0u);
+  return true;
 }
 
 // ---------------------------------------------------------------- dtypes
@@ -129,39 +170,105 @@ __device__ __forceinline__ void load_chunk(const In* __restrict__ row, int64_t c
   }
 }
 
+// Loads one 16-byte vector at element e0 of a row; elements at or beyond V
+// read as -inf and are never touched.
+template <typename In>
+__device__ __forceinline__ void load_vec(const In* __restrict__ row, int64_t e0, int V, uint4& v) {
+  constexpr int VEC = Elem<In>::VEC;
+  if (e0 + VEC <= V) {
+    v = *reinterpret_cast<const uint4*>(row + e0);
+    return;
+  }
+  v = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
+                 Elem<In>::kNegInfWord);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    if (e0 + e < V) {
+      if constexpr (sizeof(In) == 4) {
+        set_word(v, e, __float_as_uint(row[e0 + e]));
+      } else {
+        const uint32_t h = row[e0 + e];
+        const uint32_t w = word_of(v, e >> 1);
+        set_word(v, e >> 1, (e & 1) ? ((w & 0xffffu) | (h << 16)) : ((w & 0xffff0000u) | h));
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- wave ops
-// Butterfly reductions: every lane ends with the same value (the operations
-// are commutative, so each lane's pairwise tree gives identical bits).
+// Cross-lane operations use DPP lane permutations inside each row of 16
+// lanes (quad swaps, half-row and row mirrors, row shifts) and v_readlane to
+// combine the four rows, so every lane ends with the same value.  They must
+// be called with all 64 lanes active.
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  return __hiloint2double(dpp_i<CTRL>(__double2hiint(x)), dpp_i<CTRL>(__double2loint(x)));
+}
+__device__ __forceinline__ int readlane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                          __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+
+// Reduce within each row of 16 lanes (commutative op), then across the rows.
+#define SV_ROW_REDUCE(T, DPP, OP, x)                  \
+  x = OP(x, DPP<kDppQuadXor1>(x));                    \
+  x = OP(x, DPP<kDppQuadXor2>(x));                    \
+  x = OP(x, DPP<kDppRowHalfMirror>(x));               \
+  x = OP(x, DPP<kDppRowMirror>(x));
+
+__device__ __forceinline__ float op_maxf(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ int op_mini(int a, int b) { return min(a, b); }
+__device__ __forceinline__ int op_maxi(int a, int b) { return max(a, b); }
+__device__ __forceinline__ double op_addd(double a, double b) { return a + b; }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  SV_ROW_REDUCE(float, dpp_f, op_maxf, x)
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)),
+               fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 __device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
+  SV_ROW_REDUCE(int, dpp_i, op_mini, x)
+  return min(min(readlane_i(x, 0), readlane_i(x, 16)), min(readlane_i(x, 32), readlane_i(x, 48)));
 }
 __device__ __forceinline__ int wave_max_int(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
+  SV_ROW_REDUCE(int, dpp_i, op_maxi, x)
+  return max(max(readlane_i(x, 0), readlane_i(x, 16)), max(readlane_i(x, 32), readlane_i(x, 48)));
 }
+// Sum in a fixed order (pairwise inside rows, then (r0 + r1) + (r2 + r3)).
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  SV_ROW_REDUCE(double, dpp_d, op_addd, x)
+  return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
 }
-// Inclusive prefix sum over lanes (Hillis-Steele), fixed order.
+// Inclusive prefix sum over lanes: Hillis-Steele inside each row of 16,
+// then each row adds the totals of the rows before it.
 __device__ __forceinline__ double wave_inclusive_scan(double x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kLanes; o <<= 1) {
-    const double y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
+  x += dpp_d<kDppRowShr1>(x);
+  x += dpp_d<kDppRowShr2>(x);
+  x += dpp_d<kDppRowShr4>(x);
+  x += dpp_d<kDppRowShr8>(x);
+  const double t0 = readlane_d(x, 15), t1 = readlane_d(x, 31), t2 = readlane_d(x, 47);
+  const int row = lane_id() >> 4;
+  const double off = row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+  return x + off;
 }
 
 // Ranking key of fork candidates: higher logit first, lower id on ties.
@@ -170,14 +277,29 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
 // Wave-wide best (v, i) by `better`; all lanes get the result.
 __device__ __forceinline__ void wave_best(float& v, int& i) {
+  best_step<kDppQuadXor1>(v, i);
+  best_step<kDppQuadXor2>(v, i);
+  best_step<kDppRowHalfMirror>(v, i);
+  best_step<kDppRowMirror>(v, i);
+  float bv = readlane_f(v, 0);
+  int bi = readlane_i(i, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  for (int r = 16; r < 64; r += 16) {
+    const float rv = readlane_f(v, r);
+    const int ri = readlane_i(i, r);
+    if (better(rv, ri, bv, bi)) { bv = rv; bi = ri; }
   }
+  v = bv;
+  i = bi;
 }
 
 // Sorted per-lane list of the F best candidates (best first).

@@ -300,3 +300,32 @@ def softmax_temp(logits, temperature, rows_per_temp: int = 1,
         _ptr(buf), buf.numel(), _stream_handle(stream))
     _check(code, "sv_softmax_temp")
     return out
+
+
+class PreparedVerify:
+    """sv_verify with every argument marshalled once, for issuing the same
+    call repeatedly (benchmark loops): calling it only forwards the prepared
+    pointers to the library."""
+
+    def __init__(self, target, draft, draft_tokens, temperature, u_accept, u_recover,
+                 f: int, out: dict, workspace: Workspace, stream=None):
+        self._keep = (target, draft, draft_tokens, temperature, u_accept, u_recover, out)
+        self.batch = _batch(target, draft, draft_tokens, temperature)
+        B, k = self.batch.B, self.batch.k
+        _f32(u_accept, (B, k), "u_accept")
+        _f32(u_recover, (B, k + 1), "u_recover")
+        self.forks = SvForks(int(f), out["fork_tokens"].data_ptr(),
+                             out["fork_probs"].data_ptr()) if f > 0 else None
+        buf = workspace.get(workspace_size(B, k, self.batch.V, f))
+        self._buf = buf
+        self.args = [
+            ctypes.byref(self.batch), _ptr(u_accept), _ptr(u_recover), _ptr(out["accept_len"]),
+            _ptr(out["out_token"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+            ctypes.byref(self.forks) if self.forks is not None else None,
+            _ptr(buf), ctypes.c_size_t(buf.numel()), _stream_handle(stream)]
+        self.fn = lib().sv_verify_ex
+
+    def __call__(self, opts: Optional[SvOpts] = None) -> None:
+        code = self.fn(*self.args, ctypes.byref(opts) if opts is not None else None)
+        if code != SV_OK:
+            _check(code, "sv_verify")
