@@ -44,10 +44,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--cpu-seqs", type=int, default=16,
+    ap.add_argument("--cpu-seqs", type=int, default=64,
                     help="sequences of the workload the oracle is timed on")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of the logits' size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE; runs made with --copy-calib) into the "
+                         "per-launch HBM traffic of the statistics kernel and write it to "
+                         + os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
 
 
@@ -92,6 +97,50 @@ def alg_bytes(B, k, V, f, elem):
     return logits + small_in + out, stats_kernel
 
 
+def counter_means(path, counter):
+    """Mean value per dispatch of one counter, by kernel-name prefix, from a
+    rocprofv3 counter_collection.csv (one row per dispatch and counter)."""
+    import csv
+    acc = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("k_stats" if "sv::k_stats" in name else
+                   "copy" if "neg_kernel_cuda" in name else None)
+            if key is None:
+                continue
+            s_, n_ = acc.get(key, (0.0, 0))
+            acc[key] = (s_ + float(r["Counter_Value"]), n_ + 1)
+    return {k_: v[0] / v[1] for k_, v in acc.items()}
+
+
+def write_traffic(fetch_csv, write_csv):
+    """HBM bytes per launch of the statistics kernel.  Each counter is scaled
+    by what it reads for the plain copy kernel (torch.neg over a float32
+    tensor of COPY_BYTES, which reads and writes COPY_BYTES once each)."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[WORKLOAD]
+    copy_bytes = (alg_bytes(cfg.B, cfg.k, cfg.V, cfg.f, 2)[0] // 8) * 4
+    fe = counter_means(fetch_csv, "FETCH_SIZE")
+    wr = counter_means(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (fe["copy"] * 1024.0)
+    w_scale = copy_bytes / (wr["copy"] * 1024.0)
+    fetch_b = fe["k_stats"] * 1024.0 * f_scale
+    write_b = wr["k_stats"] * 1024.0 * w_scale
+    out = {"kernel": "k_stats", "kernel_hash": kernel_hash(),
+           "bytes_per_launch": fetch_b + write_b,
+           "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "fetch_kib_raw": fe["k_stats"], "write_kib_raw": wr["k_stats"],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_bytes": copy_bytes}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(w, nseq):
     import oracle
 
@@ -108,6 +157,9 @@ def cpu_baseline(w, nseq):
 
 def main():
     a = parse()
+    if a.traffic_from:
+        write_traffic(*a.traffic_from)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; "
                                    "--gpus must be 1 (the step has no multi-GPU path)"}))
