@@ -59,10 +59,13 @@
  * in bounds).
  *
  * Workspace.  Every compute call takes a device workspace of at least
- * sv_workspace_size() bytes.  It must be zero-filled before its first use
- * (sv_workspace_init, or any zero fill); every call leaves it zero-filled in
- * the parts that must start at zero.  Calls that share a workspace must not
- * overlap in time (use one workspace per stream).
+ * sv_workspace_size() bytes.  It must be zero-filled (sv_workspace_init, or
+ * any zero fill) before its first use, and again before a call whose entry
+ * point or sizes (B, k, V, f; rows for sv_softmax_temp) differ from those of
+ * the previous call on it: where its arrival counters sit depends on them.
+ * A call leaves the workspace ready for the next call of the same kind.
+ * Calls that share a workspace must not overlap in time (use one workspace
+ * per stream).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H

@@ -40,6 +40,11 @@ constexpr double kLog2e = 1.4426950408889634074;
 
 enum Mode : int { kVerify = 0, kForks = 1, kResidual = 2, kSoftmax = 3 };
 
+// Arrival counters sit 256 bytes apart: device-scope atomics to one memory
+// line are serialised, and many rows finishing together must not queue on a
+// shared line.
+constexpr int64_t kCtrStride = 64;
+
 // Per-row results of the statistics pass (72 bytes).
 struct RowRec {
   float tm;     // target row max
@@ -70,9 +75,9 @@ struct SeqRec {
 };
 
 struct Ws {
-  unsigned* row_ctr;   // [R]
-  unsigned* seq_ctr;   // [B]
-  unsigned* k2_ctr;    // [R]
+  unsigned* row_ctr;   // [R], one per kCtrStride words
+  unsigned* seq_ctr;   // [B], one per kCtrStride words
+  unsigned* k2_ctr;    // [R], one per kCtrStride words
   float* tm; double* ts; int* targ;     // [R * cpr] target chunk partials
   float* dm; double* ds; int* darg;     // [R * cpr] draft chunk partials
   float* dtv; int* dti;                 // [R * cpr * F] draft chunk top-f
@@ -414,7 +419,7 @@ __device__ __forceinline__ void row_merge(const Params& P, int64_t slot, int b, 
 
   if (P.mode == kSoftmax) return;
   const unsigned rows_per_seq = (P.mode == kResidual && !P.rows_all) ? 1u : (unsigned)K1;
-  if (!arrive_last(&W.seq_ctr[b], rows_per_seq)) return;
+  if (!arrive_last(&W.seq_ctr[(int64_t)b * kCtrStride], rows_per_seq)) return;
   finalize_sequence(P, b);
 }
 
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(kBlock) SV_STATS_ATTR void k_stats(Params P) {
     }
   }
 
-  if (!arrive_last(&W.row_ctr[slot], (unsigned)P.nseg)) return;
+  if (!arrive_last(&W.row_ctr[slot * kCtrStride], (unsigned)P.nseg)) return;
   row_merge<In, F>(P, slot, b, j, tau, pl);
 }
 
@@ -858,7 +863,7 @@ __global__ __launch_bounds__(kBlock) void k_resid(Params P) {
       st_dev(P.ws.kp + sbase + u, sp);
     }
   }
-  if (!arrive_last(&P.ws.k2_ctr[slot], (unsigned)P.cpr)) return;
+  if (!arrive_last(&P.ws.k2_ctr[slot * kCtrStride], (unsigned)P.cpr)) return;
 
   // Row totals, in chunk order.
   const int lane = lane_id();
@@ -1001,9 +1006,9 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   const size_t RC = (size_t)(R * cpr);
   const size_t Fa = (size_t)(F > 0 ? F : 1);
-  L.row_ctr = take(sizeof(unsigned) * R);
-  L.seq_ctr = take(sizeof(unsigned) * B);
-  L.k2_ctr = take(sizeof(unsigned) * R);
+  L.row_ctr = take(sizeof(unsigned) * kCtrStride * R);
+  L.seq_ctr = take(sizeof(unsigned) * kCtrStride * B);
+  L.k2_ctr = take(sizeof(unsigned) * kCtrStride * R);
   L.tm = take(sizeof(float) * RC);
   L.ts = take(sizeof(double) * RC);
   L.targ = take(sizeof(int) * RC);

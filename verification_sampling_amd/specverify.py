@@ -118,19 +118,26 @@ def _stream_handle(stream=None):
 # ------------------------------------------------------------------ workspace
 
 class Workspace:
-    """A zero-filled device buffer for the library's scratch data.  The
-    library leaves it zero-filled in the parts that must start at zero, so
-    one buffer serves any number of calls; calls sharing it must not overlap
-    (one workspace per stream)."""
+    """A device buffer for the library's scratch data.  Each call leaves it
+    ready for the next call of the same kind (entry point and sizes); the
+    counters it holds move with the sizes, so the buffer is zero-filled again
+    whenever the kind changes.  Calls sharing it must not overlap (one
+    workspace per stream)."""
 
     def __init__(self, device=None):
         self.device = torch.device("cuda") if device is None else torch.device(device)
         self.buf = None
+        self.kind = None
 
-    def get(self, nbytes: int) -> torch.Tensor:
-        if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8,
+    def get(self, nbytes: int, kind=None, stream=None) -> torch.Tensor:
+        fresh = self.buf is None or self.buf.numel() < nbytes
+        if fresh:
+            self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
                                    device=self.device)
+        if fresh or kind != self.kind:
+            _check(lib().sv_workspace_init(_ptr(self.buf), self.buf.numel(),
+                                           _stream_handle(stream)), "sv_workspace_init")
+        self.kind = kind
         return self.buf
 
 
@@ -218,8 +225,7 @@ def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int
     if f > 0:
         forks = SvForks(int(f), out["fork_tokens"].data_ptr(), out["fork_probs"].data_ptr())
     ws = workspace or default_workspace(dev, stream)
-    need = workspace_size(B, k, b.V, f)
-    buf = ws.get(need)
+    buf = ws.get(workspace_size(B, k, b.V, f), ("verify", B, k, b.V, f), stream)
     opts = None
     if timing_events is not None:
         opts = SvOpts(timing_events[0], timing_events[1])
@@ -253,7 +259,7 @@ def residual_sample(target, draft, draft_tokens, temperature, position, u_recove
         rs0, rs1 = res.stride(0), res.stride(1)
         out["residual"] = res
     ws = workspace or default_workspace(dev, stream)
-    buf = ws.get(workspace_size(B, k, V, 0))
+    buf = ws.get(workspace_size(B, k, V, 0), ("residual", B, k, V), stream)
     code = lib().sv_residual_sample(
         ctypes.byref(b), _ptr(position), _ptr(u_recover), _ptr(out["token"]),
         ctypes.c_void_p(res.data_ptr()) if res is not None else None, rs0, rs1,
@@ -273,7 +279,7 @@ def forked_topf(draft, draft_tokens, temperature, f: int,
     probs = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
     forks = SvForks(int(f), toks.data_ptr(), probs.data_ptr())
     ws = workspace or default_workspace(dev, stream)
-    buf = ws.get(workspace_size(B, k, b.V, f))
+    buf = ws.get(workspace_size(B, k, b.V, f), ("forks", B, k, b.V, f), stream)
     code = lib().sv_forked_topf(ctypes.byref(b), ctypes.byref(forks), _ptr(buf),
                                 buf.numel(), _stream_handle(stream))
     _check(code, "sv_forked_topf")
@@ -293,7 +299,7 @@ def softmax_temp(logits, temperature, rows_per_temp: int = 1,
     Vp = (V + 3) // 4 * 4
     out = torch.empty(rows, Vp, dtype=torch.float32, device=dev)[:, :V]
     ws = workspace or default_workspace(dev, stream)
-    buf = ws.get(workspace_size(rows, 0, V, 0))
+    buf = ws.get(workspace_size(rows, 0, V, 0), ("softmax", rows, V), stream)
     code = lib().sv_softmax_temp(
         _ptr(logits), _dtype_code(logits), int(rows), int(V), logits.stride(0),
         _ptr(temperature), int(rows_per_temp), ctypes.c_void_p(out.data_ptr()), out.stride(0),
@@ -316,7 +322,8 @@ class PreparedVerify:
         _f32(u_recover, (B, k + 1), "u_recover")
         self.forks = SvForks(int(f), out["fork_tokens"].data_ptr(),
                              out["fork_probs"].data_ptr()) if f > 0 else None
-        buf = workspace.get(workspace_size(B, k, self.batch.V, f))
+        buf = workspace.get(workspace_size(B, k, self.batch.V, f),
+                            ("verify", B, k, self.batch.V, f), stream)
         self._buf = buf
         self.args = [
             ctypes.byref(self.batch), _ptr(u_accept), _ptr(u_recover), _ptr(out["accept_len"]),
