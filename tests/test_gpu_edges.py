@@ -233,3 +233,30 @@ def test_forked_topf_standalone(sv, f):
     np.testing.assert_array_equal(toks.cpu().numpy(), rt)
     assert_probs_close(probs.cpu().numpy(), rp, "fork probs")
     log(f"[edges] forked_topf f={f}: ok")
+
+
+def test_workspace_reused_across_shapes(sv):
+    """One workspace serves calls of different sizes and entry points in
+    turn: the arrival counters move with the sizes, and every call must find
+    its own zeroed."""
+    ws = sv.Workspace(torch.device("cuda", 0))
+    shapes = [(2, 5, 33, 5, "bf16"), (6, 7, 3000, 3, "bf16"), (1, 2, 17, 0, "f32"),
+              (2, 5, 33, 5, "bf16"), (9, 3, 4097, 2, "f32"), (6, 7, 3000, 3, "bf16")]
+    for i, (B, k, V, f, dtype) in enumerate(shapes):
+        w = synth(B, k, V, dtype, 0.9, seed=4100 + i, f=f)
+        T, D = padded_dev(w.target, dtype), padded_dev(w.draft, dtype)
+        d = torch.from_numpy(w.draft_tokens).cuda()
+        tau = torch.from_numpy(w.temperature).cuda()
+        for _ in range(2):
+            out = sv.verify(T, D, d, tau, torch.from_numpy(w.u_accept).cuda(),
+                            torch.from_numpy(w.u_recover).cuda(), f=f, want_p=True, want_q=True,
+                            workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.verify_batch(w.target, w.draft, dtype, w.draft_tokens, w.temperature,
+                                      w.u_accept, w.u_recover, f=f)
+            compare_verify(out, ref, np.arange(B), f, k)
+        if f > 0:
+            toks, _ = sv.forked_topf(D, d, tau, f, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(toks, out["fork_tokens"])
+    log("[edges] workspace reused across shapes and entry points: ok")
