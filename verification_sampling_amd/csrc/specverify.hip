@@ -1,19 +1,23 @@
 // libspecverify: kernels and the C ABI entry points (gfx950).
 //
-// Kernel chain of sv_verify (one stream, no host synchronisation):
-//   k_stats   one wavefront per (row, chunk): streams the target and draft
-//             chunk once with 16-byte loads, writes chunk partials; the last
-//             wave to finish a row merges its partials (row max, sum, argmax,
-//             fork top-f, p(d), q(d)); the last row to finish a sequence
-//             decides it (acceptance tests, first rejection by ballot, greedy
-//             token).
-//   k_resid   one wavefront per chunk of row n of every sequence still to be
-//             drawn (temperature > 0): residual chunk sums in fp64; the last
-//             wave of the row finds the chunk holding u*Z and draws the token
-//             inside it.
-// sv_residual_sample runs the same pair (plus k_write for the full residual
-// distributions); sv_softmax_temp runs k_stats then k_write; sv_forked_topf
-// runs k_stats alone.
+// Kernel chain of sv_verify (one stream, no host synchronisation, no
+// device-scope atomics):
+//   k_stats   one round of resident waves; each streams one segment of
+//             consecutive slabs of one row (target and draft together,
+//             16-byte loads, the next chunk in flight while the current one
+//             is folded) and writes the segment's partial statistics: row
+//             reference, fp64 sum of exponentials, argmax at temperature 0,
+//             and the draft's top-F fork candidates with the drafted token
+//             masked out.
+//   k_decide  one 1024-thread block per sequence: its waves merge the rows'
+//             partials in LDS (row reference and sum, argmax, p(d), q(d),
+//             forks); wave 0 runs the acceptance tests and finds the first
+//             rejection by ballot; the outputs are written; for temperature
+//             > 0 the block re-reads row n, sums max(0, p - q) (or p) per
+//             chunk, and wave 0 draws the token by inverse CDF.
+// sv_residual_sample runs the same pair at given positions (plus k_write for
+// the full residual distributions); sv_softmax_temp runs k_stats then
+// k_write; sv_forked_topf runs k_stats then k_decide without draws.
 //
 // The speculative-sampling rule (accept iff u < min(1, p/q), first
 // rejection, draw from max(0, p - q), bonus draw from p_k) follows the
@@ -27,8 +31,10 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <stdint.h>
 #include <string.h>
+#include <type_traits>
 
 #include "specverify.h"
 #include "sv_device.h"
@@ -40,51 +46,41 @@ constexpr double kLog2e = 1.4426950408889634074;
 
 enum Mode : int { kVerify = 0, kForks = 1, kResidual = 2, kSoftmax = 3 };
 
+// Largest vocabulary: k_decide keeps one pair of chunk totals per chunk of a
+// row in LDS (fp32 chunks hold 1024 elements).
+constexpr int kMaxChunks = 1024;
+constexpr int64_t kMaxV = (int64_t)kMaxChunks * kU * kLanes * 4;
+constexpr int kMaxSeg = 64;  // partials per row (one lane each when merged)
+
 // Arrival counters sit 256 bytes apart: device-scope atomics to one memory
-// line are serialised, and many rows finishing together must not queue on a
-// shared line.
+// line are serialised.
 constexpr int64_t kCtrStride = 64;
 
-// Per-row results of the statistics pass (72 bytes).
+// Row record for k_write (residual distributions), written by k_decide.
 struct RowRec {
-  float tm;     // target row max
-  int targ;     // target argmax (temperature 0)
+  float tm;     // target reference
+  int targ;     // target argmax
   double ts;    // target sum of 2^((x - tm) c)
-  float dm;     // draft row max (drafted token included)
-  int darg;     // draft argmax (temperature 0)
+  float dm;     // draft reference (unmasked row)
+  int valid;
   double ds;    // draft sum of 2^((y - dm) c)
-  double pd;    // p(d), q(d) of the drafted token (j < k)
-  double qd;
-  double zr;    // residual total sum max(0, p - q) (residual kernel)
-  double zp;    // target total sum p (residual kernel)
-  int valid;    // rows read are finite and inputs in range
-  int pad;
+  double zr;    // residual total sum max(0, p - q)
+  double zp;    // target total sum p
 };
-static_assert(sizeof(RowRec) == 72, "RowRec layout");
-
-__device__ __forceinline__ void store_row(RowRec* p, const RowRec& r) {
-  st_dev(&p->tm, r.tm); st_dev(&p->targ, r.targ); st_dev(&p->ts, r.ts);
-  st_dev(&p->dm, r.dm); st_dev(&p->darg, r.darg); st_dev(&p->ds, r.ds);
-  st_dev(&p->pd, r.pd); st_dev(&p->qd, r.qd); st_dev(&p->zr, r.zr); st_dev(&p->zp, r.zp);
-  st_dev(&p->valid, r.valid); st_dev(&p->pad, r.pad);
-}
 
 struct SeqRec {
   int n;        // outcome position
-  int status;   // 0 error, 1 finished (greedy), 2 residual draw pending
+  int status;   // 0 error, 1 finished (greedy), 2 drawn at temperature > 0
 };
 
 struct Ws {
-  unsigned* row_ctr;   // [R], one per kCtrStride words
-  unsigned* seq_ctr;   // [B], one per kCtrStride words
-  unsigned* k2_ctr;    // [R], one per kCtrStride words
-  float* tm; double* ts; int* targ;     // [R * cpr] target chunk partials
-  float* dm; double* ds; int* darg;     // [R * cpr] draft chunk partials
-  float* dtv; int* dti;                 // [R * cpr * F] draft chunk top-f
-  int* ftok; float* fprob;              // [R * F] a row's forks, staged for the sequence
-  RowRec* rows;        // [R]
-  SeqRec* seqs;        // [B]
-  double* kr; double* kp;               // [R * cpr * kU] residual slab sums
+  float* tm; double* ts; int* targ;     // [R * kMaxSeg] target segment partials
+  float* dm; double* ds; int* darg;     // [R * kMaxSeg] draft segment partials
+  float* dtv; int* dti;                 // [R * kMaxSeg * F] draft segment top-F
+  RowRec* rows;                         // [R]
+  SeqRec* seqs;                         // [B]
+  double* ctr; double* ctp;             // [tasks * cpr] k_decide chunk totals
+  unsigned* cnt;                        // [tasks * kCtrStride] k_decide arrivals
 };
 
 struct Params {
@@ -95,9 +91,12 @@ struct Params {
   const float* u_acc;
   const float* u_rec;
   const int32_t* position;
-  int32_t B, k, V, f, F, cpr, mode, rows_all, want_q;
-  int32_t nseg;            // k_stats: segments per row (one wave each)
-  int32_t seg_chunks;      // k_stats: chunks per segment
+  int32_t B, k, V, f, F, mode, rows_all, want_q;
+  int32_t cpr;             // chunks per row
+  int32_t nslab;           // slabs per row
+  int32_t nseg;            // k_stats segments per row
+  int32_t nparts;          // partials per row (k_decide, k_write merge this many)
+  int32_t nbs;             // k_decide blocks per task row
   int64_t nslots;          // row slots of k_stats
   int64_t rows_per_temp;   // softmax
   int32_t* accept_len;
@@ -117,12 +116,18 @@ __device__ __forceinline__ float slot_tau(const Params& P, int64_t slot, int b) 
   return P.tau[b];
 }
 
-// Row slot -> (sequence, position) in k_stats.
+// Row slot -> (sequence, position) of k_stats.
 __device__ __forceinline__ void slot_to_bj(const Params& P, int64_t slot, int& b, int& j) {
   if (P.mode == kSoftmax) { b = (int)slot; j = 0; return; }
   if (P.mode == kResidual && !P.rows_all) { b = (int)slot; j = P.position[b]; return; }
   b = (int)(slot / (P.k + 1));
   j = (int)(slot - (int64_t)b * (P.k + 1));
+}
+
+// Slot of row (b, j) in the partial arrays.
+__device__ __forceinline__ int64_t slot_of(const Params& P, int b, int j) {
+  if (P.mode == kResidual && !P.rows_all) return b;
+  return (int64_t)b * (P.k + 1) + j;
 }
 
 template <typename In>
@@ -170,28 +175,236 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int b, int j, float
   return r;
 }
 
-// ------------------------------------------------------------ merge helpers
+// ================================================================ k_stats
+
+// The drafted token leaves the draft row's masked statistics: the element
+// is set to -inf in the lane that holds it (one chunk per row).
+template <typename In>
+struct Vec4 {
+  uint4 v[kU];
+};
+
+template <typename In>
+__device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 v3,
+                                            int64_t e_base, int64_t mask_id) {
+  constexpr int VEC = Elem<In>::VEC;
+  static_assert(kU == 4, "mask_token takes four vectors");
+  Vec4<In> r;
+  r.v[0] = v0; r.v[1] = v1; r.v[2] = v2; r.v[3] = v3;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (e_base + (int64_t)u * slab_elems<In>() + e == mask_id) set_neg_inf<In>(r.v[u], e);
+    }
+  }
+  return r;
+}
+
+struct SegState {
+  Warm tw, dw;    // temperature > 0
+  Greedy tg, dg;  // temperature 0
+  int nc;         // fork candidate slots in use (this lane)
+  float kv;       // fork candidate threshold (wave-uniform)
+};
+
+// One chunk of a segment, already in registers.  RT / RD: the target / draft
+// row is read; GREEDY: temperature 0; FIRST: the segment's first chunk.
+// cs: the chunk's first element (wave-uniform); e_base = cs + lane * VEC;
+// nv: vectors of the chunk inside the segment (the others read as -inf).
+template <typename In, int F, bool RT, bool RD, bool GREEDY, bool FIRST>
+__device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* drow,
+                                            const uint4 (&traw)[kU], uint4 (&draw)[kU],
+                                            int64_t cs, int64_t e_base, int nv, float c,
+                                            SegState& st, CandLds<F>* L) {
+  constexpr int64_t SLAB = slab_elems<In>();
+  constexpr int64_t CH = chunk_elems<In>();
+  if constexpr (RT) {
+    float vs[kU], m8[kU];
+    if constexpr (GREEDY) greedy_fold<In>(st.tg, traw, e_base, true, m8);
+    else warm_fold<In, FIRST>(st.tw, traw, c, vs, m8);
+  }
+  if constexpr (RD) {
+    if (pl.mask_id >= cs && pl.mask_id < cs + CH) {
+      const Vec4<In> m = mask_token<In>(draw[0], draw[1], draw[2], draw[3], e_base, pl.mask_id);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) draw[u] = m.v[u];
+    }
+    float vs[kU], m8[kU];
+    if constexpr (GREEDY) greedy_fold<In>(st.dg, draw, e_base, !pl.topf, m8);
+    else warm_fold<In, FIRST>(st.dw, draw, c, vs, m8);
+    if constexpr (F > 0) {
+      if (pl.topf) {
+        unsigned bits = 0;
+        if constexpr (FIRST) {
+          // every element of the chunk's top-F reaches the F-th largest lane
+          // maximum; the first chunk's candidates are the vectors there
+          float lm = m8[0];
+#pragma unroll
+          for (int u = 1; u < kU; ++u) lm = fmaxf(lm, m8[u]);
+          st.kv = wave_fth_largest<F>(lm, F);
+#pragma unroll
+          for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
+        } else if (!(st.kv > neg_inf())) {
+          bits = (1u << kU) - 1u;  // fewer than F elements seen: all are candidates
+        } else if constexpr (GREEDY) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
+        } else {
+          // an element at or above kv has a term 2^(x c - hi) of at least
+          // 2^(kv c - hi); a vector whose sum of terms is below that (less a
+          // margin for rounding) holds no such element
+          const float eth = __builtin_amdgcn_exp2f(fmaf(st.kv, c, -st.dw.hi)) * 0.999999f;
+#pragma unroll
+          for (int u = 0; u < kU; ++u) bits |= (vs[u] >= eth) ? (1u << u) : 0u;
+        }
+        bits &= (1u << nv) - 1u;  // vectors past the segment belong to the next one
+        if (__ballot(bits != 0u)) {
+          cand_append<F>(L, bits, e_base, SLAB, st.nc);
+          if (__ballot(st.nc > kCandSlots - kU))
+            cand_reduce<In, F, 2>(L, drow, V, pl.mask_id, st.nc, st.kv);
+        }
+      }
+    }
+  }
+}
+
+// A segment of slabs [s0, s1) of one row, a chunk (kU slabs) at a time; the
+// next chunk's loads are issued before the current chunk is folded.
+template <typename In, int F, bool RT, bool RD, bool GREEDY>
+__device__ __forceinline__ void stats_segment(const RowPlan& pl, int V, const In* trow,
+                                              const In* drow, int64_t s0, int64_t s1, float c,
+                                              SegState& st, CandLds<F>* L) {
+  constexpr int64_t SLAB = slab_elems<In>();
+  constexpr int VEC = Elem<In>::VEC;
+  const int lane = lane_id();
+  const int64_t nch = (s1 - s0 + kU - 1) / kU;
+  const int64_t slim = min(s1, (int64_t)V / SLAB);  // slabs [.., slim) lie inside the row
+  uint4 ta[kU], da[kU], tb[kU], db[kU];
+  auto load = [&](uint4 (&t)[kU], uint4 (&d)[kU], int64_t i) {
+    const int64_t sl = s0 + i * kU;
+    const int nv = (int)min<int64_t>(kU, s1 - sl);
+    const bool full = sl + kU <= slim;
+    const int64_t eb = sl * SLAB + lane * VEC;
+    if constexpr (RT) load_chunk<In>(trow, eb, nv, V, full, t);
+    if constexpr (RD) load_chunk<In>(drow, eb, nv, V, full, d);
+  };
+  auto fold = [&](const uint4 (&t)[kU], uint4 (&d)[kU], int64_t i, auto first) {
+    const int64_t sl = s0 + i * kU;
+    const int nv = (int)min<int64_t>(kU, s1 - sl);
+    stats_chunk<In, F, RT, RD, GREEDY, decltype(first)::value>(pl, V, drow, t, d, sl * SLAB,
+                                                               sl * SLAB + lane * VEC, nv, c,
+                                                               st, L);
+  };
+  load(ta, da, 0);
+  if (nch > 1) load(tb, db, 1);
+  fold(ta, da, 0, std::true_type{});
+  for (int64_t i = 1; i < nch; i += 2) {
+    if (i + 1 < nch) load(ta, da, i + 1);
+    fold(tb, db, i, std::false_type{});
+    if (i + 1 >= nch) break;
+    if (i + 2 < nch) load(tb, db, i + 2);
+    fold(ta, da, i + 1, std::false_type{});
+  }
+}
+
+// Four resident waves per SIMD: enough bytes in flight with the one-chunk
+// prefetch, and the register budget (128) the folding code needs.
+#ifndef SV_STATS_WAVES_PER_EU
+#define SV_STATS_WAVES_PER_EU 4
+#endif
+
+template <typename In, int F>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params P) {
+  const int64_t task = wave_global_id();
+  if (task >= P.nslots * P.nseg) return;
+  const int64_t slot = task / P.nseg;
+  const int seg = (int)(task - slot * P.nseg);
+  int b, j;
+  slot_to_bj(P, slot, b, j);
+  b = uniform(b);
+  j = uniform(j);
+  const float tau = uniform(slot_tau(P, slot, b));
+  const RowPlan pl = plan_row(P, b, j, tau);
+  const float c = pl.greedy ? 0.0f : scale_of(tau);
+  const int lane = lane_id();
+  const Ws& W = P.ws;
+  const int64_t s0 = (int64_t)seg * P.nslab / P.nseg;
+  const int64_t s1 = (int64_t)(seg + 1) * P.nslab / P.nseg;
+  const In* trow = pl.readT ? trow_ptr<In>(P, b, j) : nullptr;
+  const In* drow = pl.readD ? drow_ptr<In>(P, b, j) : nullptr;
+
+  __shared__ CandLds<F> s_cand[kWavesPerBlock];
+  CandLds<F>* L = &s_cand[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+  SegState st;
+  warm_init(st.tw); warm_init(st.dw);
+  greedy_init(st.tg); greedy_init(st.dg);
+  st.nc = 0;
+  st.kv = neg_inf();
+  if constexpr (F > 0) {
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < F; ++r) { L->wv[r] = neg_inf(); L->wi[r] = kEmptyId; }
+    }
+  }
+  if (s1 > s0) {
+    const int V = P.V;
+    if (pl.readT && pl.readD) {
+      if (pl.greedy) stats_segment<In, F, true, true, true>(pl, V, trow, drow, s0, s1, c, st, L);
+      else stats_segment<In, F, true, true, false>(pl, V, trow, drow, s0, s1, c, st, L);
+    } else if (pl.readT) {
+      if (pl.greedy) stats_segment<In, F, true, false, true>(pl, V, trow, drow, s0, s1, c, st, L);
+      else stats_segment<In, F, true, false, false>(pl, V, trow, drow, s0, s1, c, st, L);
+    } else if (pl.readD) {
+      if (pl.greedy) stats_segment<In, F, false, true, true>(pl, V, trow, drow, s0, s1, c, st, L);
+      else stats_segment<In, F, false, true, false>(pl, V, trow, drow, s0, s1, c, st, L);
+    }
+  }
+  if constexpr (F > 0) {
+    if (pl.topf && pl.readD) cand_reduce<In, F, kCandSlots>(L, drow, P.V, pl.mask_id, st.nc, st.kv);
+  }
+
+  const int64_t part = slot * kMaxSeg + seg;
+  if (pl.readT) {
+    const WaveStats w = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
+    if (lane == 0) { W.tm[part] = w.m; W.ts[part] = w.s; W.targ[part] = w.arg; }
+  }
+  if (pl.readD) {
+    const WaveStats w = pl.greedy ? wave_finish_greedy(st.dg) : wave_finish_warm(st.dw, c);
+    if (lane == 0) { W.dm[part] = w.m; W.ds[part] = w.s; W.darg[part] = w.arg; }
+    if constexpr (F > 0) {
+      if (pl.topf && lane < F) {
+        W.dtv[part * F + lane] = L->wv[lane];
+        W.dti[part * F + lane] = L->wi[lane];
+      }
+    }
+  }
+}
+
+// ================================================================ merging
 
 struct Merged {
   float m; double s; int arg;
 };
 
-// Row max / sum / argmax from the chunk partials of one slot.
-__device__ __forceinline__ Merged merge_chunks(const float* pm, const double* ps, const int* parg,
-                                               int64_t base, int cpr, bool greedy, double cd) {
+// Row reference / sum / argmax from the segment partials of one slot; every
+// lane gets the result.  (k_write; k_decide merges from registers.)
+__device__ __forceinline__ Merged merge_partials(const float* pm, const double* ps,
+                                                 const int* parg, int64_t base, int np,
+                                                 bool greedy, double cd) {
   const int lane = lane_id();
-  float m = neg_inf();
-  for (int ch = lane; ch < cpr; ch += kLanes) m = fmaxf(m, ld_dev(pm + base + ch));
-  const float M = wave_max(m);
+  float mi = neg_inf();
+  double si = 0.0;
+  int ai = kEmptyId;
+  if (lane < np) { mi = pm[base + lane]; si = ps[base + lane]; ai = parg[base + lane]; }
+  const float M = wave_max(mi);
   double s = 0.0;
   int arg = kEmptyId;
-  for (int ch = lane; ch < cpr; ch += kLanes) {
-    const float mc = ld_dev(pm + base + ch);
-    if (greedy) {
-      if (mc == M) arg = min(arg, ld_dev(parg + base + ch));
-    } else if (finitef(M) && mc > neg_inf()) {
-      s += ld_dev(ps + base + ch) * exp2(((double)mc - (double)M) * cd);
-    }
+  if (greedy) {
+    if (lane < np && mi == M) arg = ai;
+  } else if (finitef(M) && mi > neg_inf()) {
+    s = si * exp2(((double)mi - (double)M) * cd);
   }
   Merged r;
   r.m = M;
@@ -199,6 +412,245 @@ __device__ __forceinline__ Merged merge_chunks(const float* pm, const double* ps
   r.arg = wave_min(arg);
   return r;
 }
+
+// The same from values already in the lanes (lane i holds partial i, empty
+// lanes hold -inf).
+__device__ __forceinline__ Merged merge_lanes(float mi, double si, int ai, bool greedy, double cd) {
+  const float M = wave_max(mi);
+  double s = 0.0;
+  int arg = kEmptyId;
+  if (greedy) {
+    if (mi == M) arg = ai;
+  } else if (finitef(M) && mi > neg_inf()) {
+    s = si * exp2(((double)mi - (double)M) * cd);
+  }
+  Merged r;
+  r.m = M;
+  r.s = wave_sum(s);
+  r.arg = wave_min(arg);
+  return r;
+}
+
+// A row's merged statistics (LDS, one per row of the sequence).
+struct RowStat {
+  float tm; int targ; double ts;   // target reference, argmax, sum
+  float dm; int darg; double ds;   // draft (unmasked row)
+  double pd, qd;                   // p(d), q(d) for j < k
+  int valid;
+  int ftok[kMaxF];                 // forks (f entries)
+  float fprob[kMaxF];
+};
+
+// Merges the partials of row (b, j) into rs (written by lanes 0..f-1 and
+// lane 0).  One wave; every load is issued before the first is used.
+template <typename In, int F>
+__device__ __forceinline__ void row_stat(const Params& P, int b, int j, float tau, RowStat* rs) {
+  const int lane = lane_id();
+  const RowPlan pl = plan_row(P, b, j, tau);
+  const float c = pl.greedy ? 0.0f : scale_of(tau);
+  const double cd = (double)c;
+  const Ws& W = P.ws;
+  const int k = P.k;
+  const int np = P.nparts;
+  const int64_t base = slot_of(P, b, j) * kMaxSeg;
+  const float nan = __uint_as_float(0x7fc00000u);
+
+  int d = -1;
+  bool d_ok = false;
+  if (P.mode != kSoftmax && pl.pos_ok && j < k) {
+    d = P.drafts[(int64_t)b * k + j];
+    d_ok = (d >= 0 && d < P.V);
+  }
+  // loads: partials (lane i < np: partial i), fork lists, x_d and y_d
+  float tmi = neg_inf(), dmi = neg_inf();
+  double tsi = 0.0, dsi = 0.0;
+  int tai = kEmptyId, dai = kEmptyId;
+  float lv[F > 0 ? F : 1];
+  int li[F > 0 ? F : 1];
+#pragma unroll
+  for (int r = 0; r < (F > 0 ? F : 1); ++r) { lv[r] = neg_inf(); li[r] = kEmptyId; }
+  if (lane < np) {
+    const int64_t e = base + lane;
+    if (pl.readT) { tmi = W.tm[e]; tsi = W.ts[e]; tai = W.targ[e]; }
+    if (pl.readD) {
+      dmi = W.dm[e]; dsi = W.ds[e]; dai = W.darg[e];
+      if constexpr (F > 0) {
+        if (pl.topf) {
+#pragma unroll
+          for (int r = 0; r < F; ++r) { lv[r] = W.dtv[e * F + r]; li[r] = W.dti[e * F + r]; }
+        }
+      }
+    }
+  }
+  float xd = 0.0f, yd = 0.0f;
+  if (d_ok) {
+    if (pl.readT) xd = load_logit<In>(trow_ptr<In>(P, b, j), d);
+    if (pl.readD) yd = load_logit<In>(drow_ptr<In>(P, b, j), d);
+  }
+
+  float tm = neg_inf(), dm = neg_inf();
+  int targ = kEmptyId, darg = kEmptyId;
+  double ts = 0.0, ds = 0.0, pd = nan, qd = nan;
+  bool valid = pl.tok && pl.pos_ok;
+
+  if (pl.readT) {
+    const Merged t = merge_lanes(tmi, tsi, tai, pl.greedy, cd);
+    tm = t.m; ts = t.s; targ = t.arg;
+    valid = valid && finitef(t.m);
+  }
+
+  TopList<F> top;
+  top.clear();
+  if (pl.readD) {
+    const Merged q = merge_lanes(dmi, dsi, dai, pl.greedy, cd);
+    if (pl.topf) {
+      if constexpr (F > 0) {
+        // the segments' lists hold the row's top-f (masked)
+        TopList<F> mine;
+        mine.clear();
+#pragma unroll
+        for (int r = 0; r < F; ++r) mine.insert(lv[r], li[r]);
+        wave_merge_lists<F>(mine, P.f, top);
+        // masked softmax at tau of the selected tokens: 2^((v - m') c) / S',
+        // lane r computes entry r
+        float v = neg_inf();
+        int id = kEmptyId;
+#pragma unroll
+        for (int r = 0; r < F; ++r) {
+          if (lane == r) { v = top.v[r]; id = top.i[r]; }
+        }
+        if (lane < P.f) {
+          float pr;
+          if (pl.greedy) pr = (lane == 0) ? 1.0f : 0.0f;
+          else if (!finitef(q.m) || !(v > neg_inf())) pr = 0.0f;
+          else pr = (float)(exp2(((double)v - (double)q.m) * cd) / q.s);
+          rs->ftok[lane] = id;
+          rs->fprob[lane] = pr;
+        }
+      }
+      if (j < k) {
+        // unmasked draft statistics from the masked ones and y_d
+        if (d_ok) {
+          const float mfull = fmaxf(q.m, yd);
+          dm = mfull;
+          if (!pl.greedy && finitef(mfull)) {
+            double s = exp2(((double)yd - (double)mfull) * cd);
+            if (q.m > neg_inf()) s += q.s * exp2(((double)q.m - (double)mfull) * cd);
+            ds = s;
+          }
+          darg = better(yd, d, top.v[0], top.i[0]) ? d : top.i[0];
+        }
+        valid = valid && d_ok && finitef(dm);
+      } else {
+        dm = q.m; ds = q.s; darg = top.i[0];
+        valid = valid && finitef(q.m);
+      }
+    } else {
+      dm = q.m; ds = q.s; darg = q.arg;
+      valid = valid && finitef(q.m);
+    }
+  }
+
+  // p(d), q(d) for the acceptance test and the optional outputs
+  if (P.mode == kVerify && j < k) {
+    valid = valid && d_ok;
+    if (valid) {
+      if (pl.greedy) {
+        pd = (d == targ) ? 1.0 : 0.0;
+        qd = pl.readD ? ((d == darg) ? 1.0 : 0.0) : (double)nan;
+      } else {
+        pd = exp2(((double)xd - (double)tm) * cd) / ts;
+        qd = exp2(((double)yd - (double)dm) * cd) / ds;
+      }
+    }
+  }
+  if (lane == 0) {
+    rs->tm = tm; rs->targ = targ; rs->ts = ts;
+    rs->dm = dm; rs->darg = darg; rs->ds = ds;
+    rs->pd = pd; rs->qd = qd;
+    rs->valid = valid ? 1 : 0;
+  }
+}
+
+// ================================================================ residual
+
+// Per-element residual weight r = max(0, p - q) and target probability p
+// from the merged row statistics (fp32 terms; references split exactly as
+// in the statistics pass).
+struct ResidCoef {
+  float c, thi, tscale, dhi, dscale;
+  bool has_q;
+};
+
+__device__ __forceinline__ ResidCoef resid_coef(float tm, double ts, float dm, double ds,
+                                                float c, bool has_q) {
+  ResidCoef k;
+  k.c = c;
+  k.thi = tm * c;
+  const float tlo = fmaf(tm, c, -k.thi);
+  k.tscale = (float)(exp2(-(double)tlo) / ts);
+  k.has_q = has_q;
+  k.dhi = 0.0f;
+  k.dscale = 0.0f;
+  if (has_q) {
+    k.dhi = dm * c;
+    const float dlo = fmaf(dm, c, -k.dhi);
+    k.dscale = (float)(exp2(-(double)dlo) / ds);
+  }
+  return k;
+}
+
+__device__ __forceinline__ void resid_elem(const ResidCoef& k, float x, float y, float& p,
+                                           float& r) {
+  p = __builtin_amdgcn_exp2f(fmaf(x, k.c, -k.thi)) * k.tscale;
+  if (k.has_q) {
+    const float q = __builtin_amdgcn_exp2f(fmaf(y, k.c, -k.dhi)) * k.dscale;
+    r = fmaxf(p - q, 0.0f);
+  } else {
+    r = p;
+  }
+}
+
+// Pairwise fp32 sum of one vector's weights (fixed order).
+template <int N>
+__device__ __forceinline__ float vec_sum(const float (&w)[N]) {
+  float a[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) a[e] = w[e];
+#pragma unroll
+  for (int h = N / 2; h > 0; h >>= 1) {
+#pragma unroll
+    for (int e = 0; e < h; ++e) a[e] = a[e] + a[e + h];
+  }
+  return a[0];
+}
+
+// Weights of a lane's chunk: per vector, the fp32 sums of r and p.
+template <typename In>
+__device__ __forceinline__ void chunk_weights(const ResidCoef& kc, const uint4 (&t)[kU],
+                                              const uint4 (&d)[kU], float (&wr)[kU],
+                                              float (&wp)[kU]) {
+  constexpr int VEC = Elem<In>::VEC;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    float r[VEC], p[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p[e], r[e]);
+    wr[u] = vec_sum<VEC>(r);
+    wp[u] = vec_sum<VEC>(p);
+  }
+}
+
+// ================================================================ k_decide
+
+constexpr int kDecideWaves = 16;
+constexpr int kDecideBlock = kDecideWaves * kLanes;
+
+struct DecideLds {
+  RowStat rs[kMaxK + 1];
+  int n, status;
+};
 
 // Overwrites the per-sequence outputs of an error sequence.
 __device__ __forceinline__ void write_seq_error(const Params& P, int b) {
@@ -223,8 +675,12 @@ __device__ __forceinline__ void write_seq_error(const Params& P, int b) {
   }
 }
 
-// The last row of sequence b to finish decides it.
-__device__ __forceinline__ void finalize_sequence(const Params& P, int b) {
+// Wave 0 of a k_decide block: validity, acceptance tests, first rejection
+// (ballot over positions) and, when write_outputs, the per-sequence outputs.
+// Returns the outcome position n and the status (0 error, 1 finished,
+// 2 draw pending).
+__device__ __forceinline__ void decide_sequence(const Params& P, int b, const DecideLds& S,
+                                                bool write_outputs, int& n_out, int& status) {
   const int lane = lane_id();
   const int k = P.k;
   const int K1 = k + 1;
@@ -232,7 +688,6 @@ __device__ __forceinline__ void finalize_sequence(const Params& P, int b) {
   const bool tok = tau_ok(tau);
   const bool greedy = tau == 0.0f;
 
-  // drafted ids in range
   bool ok = tok;
   int d = 0;
   if (lane < k) {
@@ -246,501 +701,78 @@ __device__ __forceinline__ void finalize_sequence(const Params& P, int b) {
   }
   // rows read are valid
   if (P.mode == kResidual && !P.rows_all) {
-    if (lane == 0 && !ld_dev(&P.ws.rows[b].valid)) ok = false;
+    if (lane == 0 && pos >= 0 && pos <= k && !S.rs[pos].valid) ok = false;
   } else if (lane < K1) {
-    if (!ld_dev(&P.ws.rows[(int64_t)b * K1 + lane].valid)) ok = false;
+    if (!S.rs[lane].valid) ok = false;
   }
   const bool seq_ok = __ballot(!ok) == 0ull;
 
-  SeqRec sr;
-  sr.n = 0;
-  sr.status = 0;
+  n_out = 0;
+  status = 0;
   if (!seq_ok) {
-    write_seq_error(P, b);
-  } else if (P.mode == kVerify) {
+    if (write_outputs) write_seq_error(P, b);
+    return;
+  }
+  if (P.mode == kVerify) {
     bool acc = true;
     if (lane < k) {
-      const RowRec* rr = &P.ws.rows[(int64_t)b * K1 + lane];
+      const RowStat& r = S.rs[lane];
       if (greedy) {
-        acc = (d == ld_dev(&rr->targ));
+        acc = (d == r.targ);
       } else {
         // a = min(1, p/q); q = 0: a = 1 if p > 0 else 0.  Accept iff u < a.
-        const double p = ld_dev(&rr->pd), q = ld_dev(&rr->qd);
+        const double p = r.pd, q = r.qd;
         const double a = (q == 0.0) ? (p > 0.0 ? 1.0 : 0.0) : fmin(1.0, p / q);
         acc = (double)P.u_acc[(int64_t)b * k + lane] < a;
       }
-    }
-    if (lane < k) {
-      const RowRec* rr = &P.ws.rows[(int64_t)b * K1 + lane];
-      if (P.p_draft) P.p_draft[(int64_t)b * k + lane] = (float)ld_dev(&rr->pd);
-      if (P.q_draft) P.q_draft[(int64_t)b * k + lane] = (float)ld_dev(&rr->qd);
+      if (write_outputs) {
+        if (P.p_draft) P.p_draft[(int64_t)b * k + lane] = (float)r.pd;
+        if (P.q_draft) P.q_draft[(int64_t)b * k + lane] = (float)r.qd;
+      }
     }
     const unsigned long long rej = __ballot(lane < k && !acc);
     const int n = rej ? (__ffsll((long long)rej) - 1) : k;
-    sr.n = n;
+    n_out = n;
+    if (write_outputs && lane == 0) P.accept_len[b] = n;
     if (greedy) {
-      sr.status = 1;
-      if (lane == 0) P.out_token[b] = ld_dev(&P.ws.rows[(int64_t)b * K1 + n].targ);
+      status = 1;
+      if (write_outputs && lane == 0) P.out_token[b] = S.rs[n].targ;
     } else {
-      sr.status = 2;
+      status = 2;
     }
-    if (lane == 0) P.accept_len[b] = n;
   } else if (P.mode == kResidual) {
-    sr.n = pos;
+    n_out = pos;
     if (greedy) {
-      sr.status = 1;
-      const int64_t rs = P.rows_all ? (int64_t)b * K1 + pos : (int64_t)b;
-      if (lane == 0) P.out_token[b] = ld_dev(&P.ws.rows[rs].targ);
+      status = 1;
+      if (write_outputs && lane == 0) P.out_token[b] = S.rs[pos].targ;
     } else {
-      sr.status = 2;
+      status = 2;
     }
   } else {
-    sr.status = 1;
+    status = 1;
   }
-  if (seq_ok && P.fork_tok) {
-    // forks staged by the row merges: rows b*(k+1) .. b*(k+1)+k
-    for (int t = lane; t < K1 * P.f; t += kLanes) {
-      const int jj = t / P.f, r = t - jj * P.f;
-      const int64_t src = ((int64_t)b * K1 + jj) * P.F + r;
-      P.fork_tok[(int64_t)b * K1 * P.f + t] = ld_dev(P.ws.ftok + src);
-      if (P.fork_prob) P.fork_prob[(int64_t)b * K1 * P.f + t] = ld_dev(P.ws.fprob + src);
-    }
-  }
-  if (lane == 0) P.ws.seqs[b] = sr;
 }
 
-// ------------------------------------------------------------ k_stats
-
-template <typename In, int F>
-__device__ __forceinline__ void row_merge(const Params& P, int64_t slot, int b, int j, float tau,
-                          const RowPlan& pl) {
-  const int lane = lane_id();
-  const int np = P.nseg;               // one partial per segment
-  const int64_t base = slot * P.cpr;   // partial arrays have a stride of cpr per row
-  const float c = pl.greedy ? 0.0f : scale_of(tau);
-  const double cd = (double)c;
-  const Ws& W = P.ws;
-  const int k = P.k;
-  const int K1 = k + 1;
-  const float nan = __uint_as_float(0x7fc00000u);
-
-  RowRec rec;
-  rec.tm = neg_inf(); rec.targ = kEmptyId; rec.ts = 0.0;
-  rec.dm = neg_inf(); rec.darg = kEmptyId; rec.ds = 0.0;
-  rec.pd = nan; rec.qd = nan; rec.zr = 0.0; rec.zp = 0.0;
-  rec.pad = 0;
-  bool valid = pl.tok && pl.pos_ok;
-
-  int d = -1;
-  bool d_ok = false;
-  if (P.mode != kSoftmax && pl.pos_ok && j < k) {
-    d = P.drafts[(int64_t)b * k + j];
-    d_ok = (d >= 0 && d < P.V);
-  }
-
-  if (pl.readT) {
-    const Merged t = merge_chunks(W.tm, W.ts, W.targ, base, np, pl.greedy, cd);
-    rec.tm = t.m; rec.ts = t.s; rec.targ = t.arg;
-    valid = valid && finitef(t.m);
-  }
-
-  float xd = 0.0f, yd = 0.0f;
-  if (d_ok) {
-    if (pl.readT) xd = load_logit<In>(trow_ptr<In>(P, b, j), d);
-    if (pl.readD) yd = load_logit<In>(drow_ptr<In>(P, b, j), d);
-  }
-
-  if (pl.readD) {
-    const Merged q = merge_chunks(W.dm, W.ds, W.darg, base, np, pl.greedy, cd);
-    if (pl.topf) {
-      // Fork candidates: merge the chunks' lists, keep the top f.
-      TopList<F> mine;
-      mine.clear();
-      for (int ch = lane; ch < np; ch += kLanes) {
-#pragma unroll
-        for (int r = 0; r < F; ++r)
-          mine.insert(ld_dev(W.dtv + (base + ch) * F + r), ld_dev(W.dti + (base + ch) * F + r));
-      }
-      TopList<F> top;
-      wave_merge_lists<F>(mine, P.f, top);
-      // Masked softmax at tau of the selected tokens: 2^((v - m') c) / S'.
-      // Staged in the workspace; the sequence's last wave writes the outputs.
-      if (lane == 0) {
-#pragma unroll
-        for (int r = 0; r < F; ++r) {
-          if (r < P.f) {
-            float pr;
-            if (pl.greedy) pr = (r == 0) ? 1.0f : 0.0f;
-            else if (!finitef(q.m) || !(top.v[r] > neg_inf())) pr = 0.0f;
-            else pr = (float)(exp2(((double)top.v[r] - (double)q.m) * cd) / q.s);
-            st_dev(W.ftok + slot * F + r, top.i[r]);
-            st_dev(W.fprob + slot * F + r, pr);
-          }
-        }
-      }
-      if (j < k) {
-        // Unmasked draft statistics from the masked ones and y_d.
-        if (d_ok) {
-          const float mfull = fmaxf(q.m, yd);
-          rec.dm = mfull;
-          if (!pl.greedy && finitef(mfull)) {
-            double s = exp2(((double)yd - (double)mfull) * cd);
-            if (q.m > neg_inf()) s += q.s * exp2(((double)q.m - (double)mfull) * cd);
-            rec.ds = s;
-          }
-          rec.darg = (better(yd, d, top.v[0], top.i[0])) ? d : top.i[0];
-        }
-        valid = valid && d_ok && finitef(rec.dm);
-      } else {
-        rec.dm = q.m; rec.ds = q.s; rec.darg = top.i[0];
-        valid = valid && finitef(q.m);
-      }
-    } else {
-      rec.dm = q.m; rec.ds = q.s; rec.darg = q.arg;
-      valid = valid && finitef(q.m);
-    }
-  }
-
-  // p(d), q(d) for the acceptance test and the optional outputs.
-  if (P.mode == kVerify && j < k) {
-    valid = valid && d_ok;
-    if (valid) {
-      if (pl.greedy) {
-        rec.pd = (d == rec.targ) ? 1.0 : 0.0;
-        rec.qd = pl.readD ? ((d == rec.darg) ? 1.0 : 0.0) : (double)nan;
-      } else {
-        rec.pd = exp2(((double)xd - (double)rec.tm) * cd) / rec.ts;
-        rec.qd = exp2(((double)yd - (double)rec.dm) * cd) / rec.ds;
-      }
-    }
-  }
-  rec.valid = valid ? 1 : 0;
-  if (lane == 0) store_row(&W.rows[slot], rec);
-
-  if (P.mode == kSoftmax) return;
-  const unsigned rows_per_seq = (P.mode == kResidual && !P.rows_all) ? 1u : (unsigned)K1;
-  if (!arrive_last(&W.seq_ctr[(int64_t)b * kCtrStride], rows_per_seq)) return;
-  finalize_sequence(P, b);
-}
-
-// The drafted token leaves the draft row's masked statistics: the element
-// is set to -inf in the lane that holds it (rare: one chunk per row).
+// The draw by one wave: the chunk from the per-chunk totals (device-scope
+// loads), then the vector (slab by slab, lanes inside), then the element;
+// each time the first whose running total passes u*Z among positive
+// weights, or the last positive one if rounding leaves none.
 template <typename In>
-struct Vec4 {
-  uint4 v[kU];
-};
-
-template <typename In>
-__device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 v3, int64_t cstart,
-                                            int64_t mask_id) {
+__device__ __forceinline__ int resid_draw(const Params& P, const double* tot, const In* trow,
+                                          const In* drow, const ResidCoef& kc, bool use_r,
+                                          double Z, double u) {
   constexpr int VEC = Elem<In>::VEC;
-  static_assert(kU == 4, "mask_token takes four vectors");
-  Vec4<In> r;
-  r.v[0] = v0; r.v[1] = v1; r.v[2] = v2; r.v[3] = v3;
-  const int lane = lane_id();
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if (cstart + (int64_t)(u * kLanes + lane) * VEC + e == mask_id) set_neg_inf<In>(r.v[u], e);
-    }
-  }
-  return r;
-}
-
-// Fork-candidate state of one wave (the buffer lives in LDS).
-struct WaveCand {
-  float* cv;
-  int* ci;
-  CandState st;
-};
-
-// One chunk of one row segment, already in registers.  RT / RD: the target
-// / draft row is read; GREEDY: temperature 0.
-template <typename In, int F, bool RT, bool RD, bool GREEDY>
-__device__ __forceinline__ void stats_chunk(const Params& P, const RowPlan& pl, uint4 (&traw)[kU],
-                                            uint4 (&draw)[kU], int ch, bool first, float c,
-                                            LaneStats& ta, LaneStats& da, WaveCand& wc) {
-  constexpr int CH = chunk_elems<In>();
-  const int64_t cstart = (int64_t)ch * CH;
-  if constexpr (RT) {
-    if constexpr (GREEDY) {
-      float m8[kU], mc;
-      fold_greedy<In>(ta, traw, cstart, true, m8, mc);
-    } else {
-      float vs[kU], lm;
-      fold_warm<In>(ta, traw, c, first, vs, lm);
-    }
-  }
-  if constexpr (RD) {
-    if (pl.mask_id >= cstart && pl.mask_id < cstart + CH) {
-      const Vec4<In> m = mask_token<In>(draw[0], draw[1], draw[2], draw[3], cstart, pl.mask_id);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) draw[u] = m.v[u];
-    }
-    unsigned candbits = 0;
-    if constexpr (GREEDY) {
-      float m8[kU], mc;
-      fold_greedy<In>(da, draw, cstart, !pl.topf, m8, mc);
-      if constexpr (F > 0) {
-        if (pl.topf) {
-          if (first) wc.st.kv = wave_fth_largest<F>(mc, F);
-#pragma unroll
-          for (int u = 0; u < kU; ++u) candbits |= (m8[u] >= wc.st.kv) ? (1u << u) : 0u;
-        }
-      }
-    } else {
-      float vs[kU], lm;
-      fold_warm<In>(da, draw, c, first, vs, lm);
-      if constexpr (F > 0) {
-        if (pl.topf) {
-          if (first) {
-            // every element of the chunk's top-F reaches the F-th largest lane
-            // maximum; the first chunk's candidates are all its vectors there
-            wc.st.kv = wave_fth_largest<F>(lm, F);
-            candbits = 0xFu;
-          } else {
-            // an element at or above kv has a term 2^(x c - hi) of at least
-            // 2^(kv c - hi); a vector whose sum of terms is below that (less a
-            // margin for rounding) has no such element
-            const float eth = __builtin_amdgcn_exp2f(fmaf(wc.st.kv, c, -da.hi)) * 0.999999f;
-#pragma unroll
-            for (int u = 0; u < kU; ++u) candbits |= (vs[u] >= eth) ? (1u << u) : 0u;
-          }
-        }
-      }
-    }
-    if constexpr (F > 0) {
-      if (pl.topf) {
-        if (__ballot(candbits != 0u))
-          wc.st = cand_chunk<In, F>(draw[0], draw[1], draw[2], draw[3], candbits, cstart, P.V,
-                                    pl.mask_id, wc.cv, wc.ci, wc.st);
-        if (first) wc.st = cand_compact<F>(wc.cv, wc.ci, wc.st);
-      }
-    }
-  }
-}
-
-// A row segment [c0, c1): full chunks [c0, cfull), then at most one partial
-// chunk.  Target and draft loads of a chunk are issued together.
-template <typename In, int F, bool RT, bool RD, bool GREEDY>
-__device__ __forceinline__ void stats_segment(const Params& P, const RowPlan& pl, const In* trow,
-                                              const In* drow, int c0, int c1, int cfull, float c,
-                                              LaneStats& ta, LaneStats& da, WaveCand& wc) {
-  constexpr int CH = chunk_elems<In>();
-  for (int ch = c0; ch < c1; ++ch) {
-    const bool full = ch < cfull;
-    uint4 t[kU], d[kU];
-    if constexpr (RT) load_chunk<In>(trow, (int64_t)ch * CH, P.V, full, t);
-    if constexpr (RD) load_chunk<In>(drow, (int64_t)ch * CH, P.V, full, d);
-    stats_chunk<In, F, RT, RD, GREEDY>(P, pl, t, d, ch, ch == c0, c, ta, da, wc);
-  }
-}
-
-// Occupancy target of the statistics kernel (waves per SIMD); 0 leaves the
-// register budget to the compiler.
-#ifndef SV_STATS_WAVES_PER_EU
-#define SV_STATS_WAVES_PER_EU 0
-#endif
-#if SV_STATS_WAVES_PER_EU > 0
-#define SV_STATS_ATTR __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU, 8)))
-#else
-#define SV_STATS_ATTR
-#endif
-
-template <typename In, int F>
-__global__ __launch_bounds__(kBlock) SV_STATS_ATTR void k_stats(Params P) {
-  constexpr int CH = chunk_elems<In>();
-  const int64_t task = wave_global_id();
-  if (task >= P.nslots * P.nseg) return;
-  const int64_t slot = task / P.nseg;
-  const int seg = (int)(task - slot * P.nseg);
-  int b, j;
-  slot_to_bj(P, slot, b, j);
-  b = uniform(b);
-  j = uniform(j);
-  const float tau = uniform(slot_tau(P, slot, b));
-  const RowPlan pl = plan_row(P, b, j, tau);
-  const float c = pl.greedy ? 0.0f : scale_of(tau);
-  const int lane = lane_id();
-  const Ws& W = P.ws;
-  const int c0 = seg * P.seg_chunks;
-  const int c1 = min(c0 + P.seg_chunks, P.cpr);
-  const int cfull = min(c1, max(c0, P.V / CH));  // chunks [c0, cfull) lie inside the row
-  const In* trow = pl.readT ? trow_ptr<In>(P, b, j) : nullptr;
-  const In* drow = pl.readD ? drow_ptr<In>(P, b, j) : nullptr;
-
-  LaneStats ta, da;
-  lane_init(ta);
-  lane_init(da);
-  __shared__ float s_cv[kWavesPerBlock * kCandCap];
-  __shared__ int s_ci[kWavesPerBlock * kCandCap];
-  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  WaveCand cb;
-  cb.cv = s_cv + wib * kCandCap;
-  cb.ci = s_ci + wib * kCandCap;
-  cb.st.n = 0;
-  cb.st.kv = neg_inf();
-  // specialised loops: which rows are read and whether the row is greedy
-  if (pl.readT && pl.readD) {
-    if (pl.greedy) stats_segment<In, F, true, true, true>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
-    else stats_segment<In, F, true, true, false>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
-  } else if (pl.readT) {
-    if (pl.greedy) stats_segment<In, F, true, false, true>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
-    else stats_segment<In, F, true, false, false>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
-  } else if (pl.readD) {
-    if (pl.greedy) stats_segment<In, F, false, true, true>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
-    else stats_segment<In, F, false, true, false>(P, pl, trow, drow, c0, c1, cfull, c, ta, da, cb);
-  }
-  TopList<F> wl;
-  wl.clear();
-  if constexpr (F > 0) {
-    if (pl.topf) {
-      CandBuf buf;
-      buf.v = cb.cv;
-      buf.id = cb.ci;
-      buf.n = cb.st.n;
-      buf.kv = cb.st.kv;
-      cand_select<F>(buf, wl);
-    }
-  }
-
-  const int64_t part = slot * P.cpr + seg;
-  if (pl.readT) {
-    const WaveStats w = wave_finish(ta, c, pl.greedy);
-    if (lane == 0) { st_dev(W.tm + part, w.m); st_dev(W.ts + part, w.s); st_dev(W.targ + part, w.arg); }
-  }
-  if (pl.readD) {
-    const WaveStats w = wave_finish(da, c, pl.greedy);
-    if (lane == 0) {
-      st_dev(W.dm + part, w.m); st_dev(W.ds + part, w.s); st_dev(W.darg + part, w.arg);
-      if constexpr (F > 0) {
-#pragma unroll
-        for (int r = 0; r < F; ++r) {
-          st_dev(W.dtv + part * F + r, wl.v[r]);
-          st_dev(W.dti + part * F + r, wl.i[r]);
-        }
-      }
-    }
-  }
-
-  if (!arrive_last(&W.row_ctr[slot * kCtrStride], (unsigned)P.nseg)) return;
-  row_merge<In, F>(P, slot, b, j, tau, pl);
-}
-
-// ------------------------------------------------------------ k_resid
-
-// Per-element residual weight r = max(0, p - q) and target probability p,
-// from the merged row statistics (fp32; references split exactly as in
-// chunk_stats).
-struct ResidCoef {
-  float c, thi, tscale, dhi, dscale;
-  bool has_q;
-};
-
-__device__ __forceinline__ ResidCoef resid_coef(const RowRec& rr, float c, bool has_q) {
-  ResidCoef k;
-  k.c = c;
-  k.thi = rr.tm * c;
-  const float tlo = fmaf(rr.tm, c, -k.thi);
-  k.tscale = (float)(exp2(-(double)tlo) / rr.ts);
-  k.has_q = has_q;
-  k.dhi = 0.0f;
-  k.dscale = 0.0f;
-  if (has_q) {
-    k.dhi = rr.dm * c;
-    const float dlo = fmaf(rr.dm, c, -k.dhi);
-    k.dscale = (float)(exp2(-(double)dlo) / rr.ds);
-  }
-  return k;
-}
-
-__device__ __forceinline__ void resid_elem(const ResidCoef& k, float x, float y, float& p, float& r) {
-  p = __builtin_amdgcn_exp2f(fmaf(x, k.c, -k.thi)) * k.tscale;
-  if (k.has_q) {
-    const float q = __builtin_amdgcn_exp2f(fmaf(y, k.c, -k.dhi)) * k.dscale;
-    r = fmaxf(p - q, 0.0f);
-  } else {
-    r = p;
-  }
-}
-
-// Weights of one 16-byte vector: w[e] = r (residual) or p, e in element order.
-template <typename In>
-__device__ __forceinline__ void resid_vec(const ResidCoef& kc, const uint4& tv, const uint4& dv,
-                                          float (&r)[Elem<In>::VEC], float (&p)[Elem<In>::VEC]) {
-#pragma unroll
-  for (int e = 0; e < Elem<In>::VEC; ++e)
-    resid_elem(kc, elem<In>(tv, e), kc.has_q ? elem<In>(dv, e) : 0.0f, p[e], r[e]);
-}
-
-// Pairwise fp32 sum of one vector's weights (fixed order).
-template <int N>
-__device__ __forceinline__ float vec_sum(const float (&w)[N]) {
-  float a[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) a[e] = w[e];
-#pragma unroll
-  for (int h = N / 2; h > 0; h >>= 1) {
-#pragma unroll
-    for (int e = 0; e < h; ++e) a[e] = a[e] + a[e + h];
-  }
-  return a[0];
-}
-
-// k_resid slot -> (b, j, record slot).
-__device__ __forceinline__ void resid_slot(const Params& P, int64_t slot, int& b, int& j,
-                                           int64_t& rslot, bool& draw_row) {
-  const int K1 = P.k + 1;
-  if (P.mode == kResidual && P.rows_all) {
-    b = (int)(slot / K1);
-    j = (int)(slot - (int64_t)b * K1);
-    rslot = slot;
-    draw_row = (j == P.ws.seqs[b].n);
-  } else {
-    b = (int)slot;
-    j = P.ws.seqs[b].n;
-    rslot = (P.mode == kVerify) ? (int64_t)b * K1 + j : (int64_t)b;
-    draw_row = true;
-  }
-}
-
-// The draw of one row, by the wave that finished its residual sums.  Token
-// order inside a chunk is slab by slab: slab u holds vector u of lanes
-// 0..63, i.e. 64 consecutive 16-byte vectors.  The chunk holding the target
-// is found from the chunk sums, the slab from that chunk's slab sums, the
-// lane from a scan of one re-read slab, and the token inside the lane's
-// vector.  Every step keeps to tokens of positive weight: the token is the
-// first one whose running total passes u*Z, or the last positive one if
-// rounding leaves none.
-template <typename In>
-__device__ __forceinline__ void resid_draw(const Params& P, int64_t slot, int b, int j,
-                                           const ResidCoef& kc, double Zr, double Zp) {
-  constexpr int VEC = Elem<In>::VEC;
-  constexpr int CH = chunk_elems<In>();
+  constexpr int64_t SLAB = slab_elems<In>();
   const int lane = lane_id();
   const int cpr = P.cpr;
-  const bool use_r = (j < P.k) && Zr > 0.0;
-  const double Z = use_r ? Zr : Zp;
-  const double* slabs = use_r ? P.ws.kr : P.ws.kp;
-  const double target = (double)P.u_rec[(int64_t)b * (P.k + 1) + j] * Z;
-  const int64_t sbase = slot * (int64_t)cpr * kU;
+  const double target = u * Z;
 
-  // 1. chunk: first whose inclusive prefix passes the target
+  // 1. chunk
   int cstar = -1, clast = -1;
   double before = 0.0, before_last = 0.0, carry = 0.0;
-  double sl[kU], sl_last[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) { sl[u] = 0.0; sl_last[u] = 0.0; }
   for (int g = 0; g < cpr; g += kLanes) {
     const int ch = g + lane;
-    double v[kU];
-    double w = 0.0;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      v[u] = ch < cpr ? ld_dev(slabs + sbase + (int64_t)ch * kU + u) : 0.0;
-      w += v[u];
-    }
+    const double w = ch < cpr ? ld_dev(tot + ch) : 0.0;
     const double incl = carry + wave_inclusive_scan(w);
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = carry;
@@ -749,154 +781,239 @@ __device__ __forceinline__ void resid_draw(const Params& P, int64_t slot, int b,
       const int l = __ffsll((long long)hit) - 1;
       cstar = g + l;
       before = readlane_d(excl, l);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) sl[u] = readlane_d(v[u], l);
     }
     const unsigned long long posm = __ballot(ch < cpr && w > 0.0);
     if (posm) {
       const int l = 63 - __clzll((long long)posm);
       clast = g + l;
       before_last = readlane_d(excl, l);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) sl_last[u] = readlane_d(v[u], l);
     }
     carry = readlane_d(incl, kLanes - 1);
   }
-  if (cstar < 0) {
-    cstar = clast;
-    before = before_last;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) sl[u] = sl_last[u];
-  }
+  if (cstar < 0) { cstar = clast; before = before_last; }
   if (cstar < 0) { cstar = 0; before = 0.0; }
 
-  // 2. slab inside that chunk (uniform)
-  int ustar = -1, ulast = 0;
-  double ubefore = before, ubefore_last = before, run = before;
+  // 2. re-read that chunk; vector sums scanned slab by slab
+  const int64_t sl = (int64_t)cstar * kU;
+  const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
+  const int64_t eb = sl * SLAB + lane * VEC;
+  uint4 t[kU], d[kU];
+  load_chunk<In>(trow, eb, nv, P.V, false, t);
+  if (kc.has_q) {
+    load_chunk<In>(drow, eb, nv, P.V, false, d);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) d[u] = make_uint4(0, 0, 0, 0);
+  }
+  float w[kU][VEC];
+  float vsum[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    if (sl[u] > 0.0) {
-      if (ustar < 0 && run + sl[u] > target) { ustar = u; ubefore = run; }
-      ulast = u;
-      ubefore_last = run;
-    }
-    run += sl[u];
-  }
-  if (ustar < 0) { ustar = ulast; ubefore = ubefore_last; }
-
-  // 3. re-read that slab (one vector per lane) and find the lane
-  const int64_t cstart = (int64_t)cstar * CH;
-  const int64_t e0 = cstart + (int64_t)(ustar * kLanes + lane) * VEC;
-  float w[VEC];
-  {
-    uint4 tv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
-    const In* tr = trow_ptr<In>(P, b, j);
-    const In* dr = kc.has_q ? drow_ptr<In>(P, b, j) : nullptr;
-    load_vec<In>(tr, e0, P.V, tv);
-    if (kc.has_q) load_vec<In>(dr, e0, P.V, dv);
     float r[VEC], p[VEC];
-    resid_vec<In>(kc, tv, dv, r, p);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) w[e] = (e0 + e < P.V) ? (use_r ? r[e] : p[e]) : 0.0f;
+    for (int e = 0; e < VEC; ++e)
+      resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p[e], r[e]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) w[u][e] = use_r ? r[e] : p[e];
+    vsum[u] = use_r ? vec_sum<VEC>(r) : vec_sum<VEC>(p);
   }
-  const float vt = vec_sum<VEC>(w);
-  const double incl = ubefore + wave_inclusive_scan((double)vt);
-  double excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = ubefore;
-  const unsigned long long hit = __ballot(vt > 0.0f && incl > target);
-  const unsigned long long posm = __ballot(vt > 0.0f);
-  const int lstar = hit ? (__ffsll((long long)hit) - 1) : (posm ? 63 - __clzll((long long)posm) : 0);
-
-  // 4. the token inside lane lstar's vector
-  int t = -1, vlast = -1;
-  float acc = 0.0f;
+  int ustar = -1, lstar = 0, ulast = -1, llast = 0;
+  double my_ex[kU];  // this lane's running total before its vector, per slab
+  carry = before;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    acc += w[e];
-    if (w[e] > 0.0f) {
-      vlast = (int)(e0 + e);
-      if (t < 0 && excl + (double)acc > target) t = (int)(e0 + e);
+  for (int u = 0; u < kU; ++u) {
+    const double incl = carry + wave_inclusive_scan((double)vsum[u]);
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = carry;
+    my_ex[u] = excl;
+    const unsigned long long hit = __ballot(vsum[u] > 0.0f && incl > target);
+    if (ustar < 0 && hit) {
+      ustar = u;
+      lstar = __ffsll((long long)hit) - 1;
+    }
+    const unsigned long long posm = __ballot(vsum[u] > 0.0f);
+    if (posm) {
+      ulast = u;
+      llast = 63 - __clzll((long long)posm);
+    }
+    carry = readlane_d(incl, kLanes - 1);
+  }
+  if (ustar < 0) { ustar = ulast; lstar = llast; }
+  if (ustar < 0) { ustar = 0; lstar = 0; }
+
+  // 3. the element inside lane lstar's vector ustar
+  int tokv = -1;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if (u == ustar) {
+      int tk = -1, vlast = -1;
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        acc += w[u][e];
+        if (w[u][e] > 0.0f) {
+          const int id = (int)(eb + (int64_t)u * SLAB + e);
+          vlast = id;
+          if (tk < 0 && my_ex[u] + (double)acc > target) tk = id;
+        }
+      }
+      tokv = tk < 0 ? vlast : tk;
     }
   }
-  if (t < 0) t = vlast;
-  const int tok = readlane_i(t, lstar);
+  return readlane_i(tokv, lstar);
+}
+
+// P.nbs blocks per task row: a task row is a sequence (verify, forks,
+// residual at given positions) or a (sequence, position) pair (residual with
+// full distributions).  Every block of a task merges the rows' partials and
+// decides the sequence (block 0 writes the outputs); for a draw at
+// temperature > 0 the blocks split the chunks of the row to sum, publish
+// the chunk totals with device-scope stores, and the last block to arrive
+// draws the token.
+template <typename In, int F>
+__global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
+  __shared__ DecideLds S;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int K1 = P.k + 1;
+  const int64_t task = blockIdx.x / P.nbs;
+  const int part = (int)(blockIdx.x - task * P.nbs);
+  int b, jt;  // sequence, and the task's own row in the full-residual mode
+  if (P.mode == kResidual && P.rows_all) {
+    b = (int)(task / K1);
+    jt = (int)(task - (int64_t)b * K1);
+  } else {
+    b = (int)task;
+    jt = -1;
+  }
+  const float tau = P.tau[b];
+  const bool owner = jt <= 0 && part == 0;  // writes the per-sequence outputs
+
+  // 1. row statistics, one wave per row
+  if (P.mode == kResidual && !P.rows_all) {
+    if (w == 0) {
+      const int pos = P.position[b];
+      if (pos >= 0 && pos <= P.k) row_stat<In, F>(P, b, pos, tau, &S.rs[pos]);
+    }
+  } else {
+    for (int j = w; j < K1; j += kDecideWaves) row_stat<In, F>(P, b, j, tau, &S.rs[j]);
+  }
+  __syncthreads();
+
+  // 2. decision
+  if (w == 0) {
+    int n, status;
+    decide_sequence(P, b, S, owner, n, status);
+    if (lane == 0) { S.n = n; S.status = status; }
+    if (owner && lane == 0) { P.ws.seqs[b].n = n; P.ws.seqs[b].status = status; }
+  }
+  __syncthreads();
+  const int n = S.n;
+  const int status = S.status;
+
+  // 3. forks
+  if (owner && status != 0 && P.fork_tok) {
+    for (int j = w; j < K1; j += kDecideWaves) {
+      if (lane < P.f) {
+        const int64_t o = ((int64_t)b * K1 + j) * P.f + lane;
+        P.fork_tok[o] = S.rs[j].ftok[lane];
+        if (P.fork_prob) P.fork_prob[o] = S.rs[j].fprob[lane];
+      }
+    }
+  }
+  if (status != 2 || P.mode == kForks) return;
+
+  // 4. this block's chunks of the row to sum: n (verify, residual at a
+  // position) or the task's row
+  const int jr = (jt >= 0) ? jt : n;
+  const bool draw_row = (jt < 0) || (jt == n);
+  const bool has_q = jr < P.k;
+  const RowStat& R = S.rs[jr];
+  const float c = scale_of(tau);
+  const ResidCoef kc = resid_coef(R.tm, R.ts, R.dm, R.ds, c, has_q);
+  const In* trow = trow_ptr<In>(P, b, jr);
+  const In* drow = has_q ? drow_ptr<In>(P, b, jr) : nullptr;
+  double* ctr = P.ws.ctr + task * (int64_t)P.cpr;
+  double* ctp = P.ws.ctp + task * (int64_t)P.cpr;
+  {
+    constexpr int VEC = Elem<In>::VEC;
+    constexpr int64_t SLAB = slab_elems<In>();
+    const int b0 = (int)((int64_t)part * P.cpr / P.nbs);
+    const int b1 = (int)((int64_t)(part + 1) * P.cpr / P.nbs);
+    const int c0 = b0 + (int)((int64_t)w * (b1 - b0) / kDecideWaves);
+    const int c1 = b0 + (int)((int64_t)(w + 1) * (b1 - b0) / kDecideWaves);
+    const int64_t slim = (int64_t)P.V / SLAB;
+    uint4 ta[kU], da[kU], tb[kU], db[kU];
+    auto load = [&](uint4 (&t)[kU], uint4 (&d)[kU], int ch) {
+      const int64_t sl = (int64_t)ch * kU;
+      const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
+      const bool full = sl + kU <= slim;
+      const int64_t eb = sl * SLAB + lane * VEC;
+      load_chunk<In>(trow, eb, nv, P.V, full, t);
+      if (has_q) {
+        load_chunk<In>(drow, eb, nv, P.V, full, d);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) d[u] = make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto sum = [&](const uint4 (&t)[kU], const uint4 (&d)[kU], int ch) {
+      float wr[kU], wp[kU];
+      chunk_weights<In>(kc, t, d, wr, wp);
+      double lr = 0.0, lp = 0.0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) { lr += (double)wr[u]; lp += (double)wp[u]; }
+      const double cr = wave_sum(lr), cp = wave_sum(lp);
+      if (lane == 0) { st_dev(ctr + ch, cr); st_dev(ctp + ch, cp); }
+    };
+    if (c0 < c1) {
+      load(ta, da, c0);
+      if (c0 + 1 < c1) load(tb, db, c0 + 1);
+      sum(ta, da, c0);
+      for (int ch = c0 + 1; ch < c1; ch += 2) {
+        if (ch + 1 < c1) load(ta, da, ch + 1);
+        sum(tb, db, ch);
+        if (ch + 1 >= c1) break;
+        if (ch + 2 < c1) load(tb, db, ch + 2);
+        sum(ta, da, ch + 1);
+      }
+    }
+  }
+  vm_complete();
+  __syncthreads();
+  if (w != 0) return;
+  if (!arrive_last(P.ws.cnt + task * kCtrStride, (unsigned)P.nbs)) return;
+
+  // 5. the last block: totals (chunk order) and the draw
+  double zr = 0.0, zp = 0.0;
+  for (int g = 0; g < P.cpr; g += kLanes) {
+    const int ch = g + lane;
+    zr += wave_sum(ch < P.cpr ? ld_dev(ctr + ch) : 0.0);
+    zp += wave_sum(ch < P.cpr ? ld_dev(ctp + ch) : 0.0);
+  }
+  if (P.mode == kResidual && P.rows_all && lane == 0) {
+    RowRec rr;
+    rr.tm = R.tm; rr.targ = R.targ; rr.ts = R.ts;
+    rr.dm = R.dm; rr.ds = R.ds; rr.valid = R.valid;
+    rr.zr = zr; rr.zp = zp;
+    P.ws.rows[(int64_t)b * K1 + jr] = rr;
+  }
+  if (!draw_row) return;
+  const bool use_r = has_q && zr > 0.0;
+  const int tok = resid_draw<In>(P, use_r ? ctr : ctp, trow, drow, kc, use_r,
+                                 use_r ? zr : zp, (double)P.u_rec[(int64_t)b * K1 + jr]);
   if (lane == 0) P.out_token[b] = tok;
 }
 
-template <typename In>
-__global__ __launch_bounds__(kBlock) void k_resid(Params P) {
-  constexpr int CH = chunk_elems<In>();
-  constexpr int VEC = Elem<In>::VEC;
-  const int64_t task = wave_global_id();
-  const int64_t nslots = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
-  if (task >= nslots * P.cpr) return;
-  const int64_t slot = task / P.cpr;
-  const int chunk = (int)(task - slot * P.cpr);
-  int b = (int)((P.mode == kResidual && P.rows_all) ? slot / (P.k + 1) : slot);
-  b = uniform(b);
-  if (P.ws.seqs[b].status != 2) return;
-  int j;
-  int64_t rslot;
-  bool draw_row;
-  resid_slot(P, slot, b, j, rslot, draw_row);
-  j = uniform(j);
-  const RowRec rr = P.ws.rows[rslot];
-  const float c = scale_of(P.tau[b]);
-  const bool has_q = j < P.k;
-  const ResidCoef kc = resid_coef(rr, c, has_q);
+// ================================================================ k_write
 
-  const int64_t cstart = (int64_t)chunk * CH;
-  const bool full = cstart + CH <= P.V;
-  uint4 traw[kU], draw[kU];
-  load_chunk<In>(trow_ptr<In>(P, b, j), cstart, P.V, full, traw);
-  if (has_q) load_chunk<In>(drow_ptr<In>(P, b, j), cstart, P.V, full, draw);
-  // slab sums of r and p (padding reads -inf: weight 0)
-  const int64_t sbase = (slot * (int64_t)P.cpr + chunk) * kU;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    float r[VEC], p[VEC];
-    resid_vec<In>(kc, traw[u], draw[u], r, p);
-    const double sr = wave_sum((double)vec_sum<VEC>(r));
-    const double sp = wave_sum((double)vec_sum<VEC>(p));
-    if (lane_id() == 0) {
-      st_dev(P.ws.kr + sbase + u, sr);
-      st_dev(P.ws.kp + sbase + u, sp);
-    }
-  }
-  if (!arrive_last(&P.ws.k2_ctr[slot * kCtrStride], (unsigned)P.cpr)) return;
-
-  // Row totals, in chunk order.
-  const int lane = lane_id();
-  double carry_r = 0.0, carry_p = 0.0;
-  const int64_t rbase = slot * (int64_t)P.cpr * kU;
-  for (int g = 0; g < P.cpr; g += kLanes) {
-    const int ch = g + lane;
-    double wr = 0.0, wp = 0.0;
-    if (ch < P.cpr) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        wr += ld_dev(P.ws.kr + rbase + (int64_t)ch * kU + u);
-        wp += ld_dev(P.ws.kp + rbase + (int64_t)ch * kU + u);
-      }
-    }
-    carry_r = readlane_d(carry_r + wave_inclusive_scan(wr), kLanes - 1);
-    carry_p = readlane_d(carry_p + wave_inclusive_scan(wp), kLanes - 1);
-  }
-  if (lane == 0) {
-    P.ws.rows[rslot].zr = carry_r;
-    P.ws.rows[rslot].zp = carry_p;
-  }
-  if (draw_row) resid_draw<In>(P, slot, b, j, kc, carry_r, carry_p);
-}
-
-// ------------------------------------------------------------ k_write
-
-// Normalised outputs: softmax rows (sv_softmax_temp) or residual
-// distributions (sv_residual_sample).
+// Normalised outputs, one wave per chunk of a row: softmax rows
+// (sv_softmax_temp; the wave merges its row's partials) or residual
+// distributions (sv_residual_sample; from the records of k_decide).
 template <typename In>
 __global__ __launch_bounds__(kBlock) void k_write(Params P) {
   constexpr int VEC = Elem<In>::VEC;
-  constexpr int CH = chunk_elems<In>();
+  constexpr int64_t SLAB = slab_elems<In>();
   const int64_t task = wave_global_id();
   const int64_t nslots = (P.mode == kSoftmax) ? P.nslots : (int64_t)P.B * (P.k + 1);
   if (task >= nslots * P.cpr) return;
@@ -909,12 +1026,18 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
   float* orow;
   int state;  // 0 NaN, 1 one-hot, 2 values
   float tau;
+  float tm, dm = 0.0f;
+  double ts, ds = 1.0, zr = 0.0;
+  int targ;
   if (P.mode == kSoftmax) {
     b = (int)slot; j = 0;
     tau = P.tau[slot / P.rows_per_temp];
     orow = P.out + slot * P.out_row;
-    const RowRec& rr = P.ws.rows[slot];
-    state = !rr.valid ? 0 : (tau == 0.0f ? 1 : 2);
+    const bool greedy = tau == 0.0f || !tau_ok(tau);
+    const Merged t = merge_partials(P.ws.tm, P.ws.ts, P.ws.targ, slot * kMaxSeg, P.nparts, greedy,
+                                    greedy ? 0.0 : (double)scale_of(tau));
+    tm = t.m; ts = t.s; targ = t.arg;
+    state = (!tau_ok(tau) || !finitef(t.m)) ? 0 : (tau == 0.0f ? 1 : 2);
   } else {
     b = (int)(slot / (P.k + 1));
     j = (int)(slot - (int64_t)b * (P.k + 1));
@@ -922,11 +1045,23 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
     orow = P.out + (int64_t)b * P.out_seq + (int64_t)j * P.out_row;
     const int st = P.ws.seqs[b].status;
     state = (st == 0) ? 0 : (tau == 0.0f ? 1 : 2);
+    if (state == 2) {
+      const RowRec& rr = P.ws.rows[slot];
+      tm = rr.tm; ts = rr.ts; targ = rr.targ;
+      dm = rr.dm; ds = rr.ds; zr = rr.zr;
+    } else {
+      // greedy rows were not merged by k_decide: the argmax comes from the
+      // partials
+      const Merged t = merge_partials(P.ws.tm, P.ws.ts, P.ws.targ, slot * kMaxSeg, P.nparts, true,
+                                      0.0);
+      tm = t.m; ts = t.s; targ = t.arg;
+    }
   }
   b = uniform(b); j = uniform(j); state = uniform(state);
-  const RowRec rr = P.ws.rows[slot];
-  const int64_t cstart = (int64_t)chunk * CH;
-  const bool full = cstart + CH <= P.V;
+  const int64_t sl = (int64_t)chunk * kU;
+  const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
+  const bool full = sl + kU <= (int64_t)P.V / SLAB;
+  const int64_t eb = sl * SLAB + lane * VEC;
 
   uint4 traw[kU], draw[kU];
   ResidCoef kc;
@@ -934,44 +1069,46 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
   bool use_r = false;
   if (state == 2) {
     const bool has_q = (P.mode == kResidual) && j < P.k;
-    kc = resid_coef(rr, scale_of(tau), has_q);
-    use_r = has_q && rr.zr > 0.0;
-    if (use_r) inv_z = (float)(1.0 / rr.zr);
-    const In* tr = (P.mode == kSoftmax)
-        ? reinterpret_cast<const In*>(P.T) + slot * P.t_row
-        : trow_ptr<In>(P, b, j);
-    load_chunk<In>(tr, cstart, P.V, full, traw);
-    if (has_q) load_chunk<In>(drow_ptr<In>(P, b, j), cstart, P.V, full, draw);
+    kc = resid_coef(tm, ts, dm, ds, scale_of(tau), has_q);
+    use_r = has_q && zr > 0.0;
+    if (use_r) inv_z = (float)(1.0 / zr);
+    const In* tr = (P.mode == kSoftmax) ? reinterpret_cast<const In*>(P.T) + slot * P.t_row
+                                        : trow_ptr<In>(P, b, j);
+    load_chunk<In>(tr, eb, nv, P.V, full, traw);
+    if (has_q) load_chunk<In>(drow_ptr<In>(P, b, j), eb, nv, P.V, full, draw);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const int64_t e0 = cstart + (int64_t)(u * kLanes + lane) * VEC;
-    float o[VEC];
+    if (u < nv) {
+      const int64_t e0 = eb + (int64_t)u * SLAB;
+      float o[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if (state == 0) {
-        o[e] = nan;
-      } else if (state == 1) {
-        o[e] = (e0 + e == rr.targ) ? 1.0f : 0.0f;
-      } else {
-        float p, r;
-        resid_elem(kc, elem<In>(traw[u], e), kc.has_q ? elem<In>(draw[u], e) : 0.0f, p, r);
-        o[e] = use_r ? r * inv_z : p;
+      for (int e = 0; e < VEC; ++e) {
+        if (state == 0) {
+          o[e] = nan;
+        } else if (state == 1) {
+          o[e] = (e0 + e == targ) ? 1.0f : 0.0f;
+        } else {
+          float p, r;
+          resid_elem(kc, elem<In>(traw[u], e), kc.has_q ? elem<In>(draw[u], e) : 0.0f, p, r);
+          o[e] = use_r ? r * inv_z : p;
+        }
       }
-    }
-    if (full || e0 + VEC <= P.V) {
+      if (e0 + VEC <= P.V) {
 #pragma unroll
-      for (int h = 0; h < VEC; h += 4)
-        *reinterpret_cast<float4*>(orow + e0 + h) = make_float4(o[h], o[h + 1], o[h + 2], o[h + 3]);
-    } else {
+        for (int h = 0; h < VEC; h += 4)
+          *reinterpret_cast<float4*>(orow + e0 + h) =
+              make_float4(o[h], o[h + 1], o[h + 2], o[h + 3]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        if (e0 + e < P.V) orow[e0 + e] = o[e];
+        for (int e = 0; e < VEC; ++e)
+          if (e0 + e < P.V) orow[e0 + e] = o[e];
+      }
     }
   }
 }
 
-// ------------------------------------------------------------ fill
+// ================================================================ fill
 
 __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) {
   const size_t n16 = bytes / 16;
@@ -982,11 +1119,10 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) 
   if (blockIdx.x == 0 && threadIdx.x < tail) p[n16 * 16 + threadIdx.x] = 0;
 }
 
-// ------------------------------------------------------------ host side
+// ================================================================ host side
 
 struct Layout {
-  size_t row_ctr, seq_ctr, k2_ctr, tm, ts, targ, dm, ds, darg, dtv, dti, ftok, fprob, rows, seqs,
-      kr, kp, total;
+  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, ctr, ctp, cnt, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -998,31 +1134,26 @@ static int fork_F(int f) {
   return f <= 4 ? 4 : 16;
 }
 
-// Workspace layout for R row slots, B sequences, cpr chunks per row and top
-// lists of F entries.
+// Workspace layout for R row slots, B sequences and rows of cpr chunks.
 static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-  const size_t RC = (size_t)(R * cpr);
+  const size_t RS = (size_t)(R * kMaxSeg);
   const size_t Fa = (size_t)(F > 0 ? F : 1);
-  L.row_ctr = take(sizeof(unsigned) * kCtrStride * R);
-  L.seq_ctr = take(sizeof(unsigned) * kCtrStride * B);
-  L.k2_ctr = take(sizeof(unsigned) * kCtrStride * R);
-  L.tm = take(sizeof(float) * RC);
-  L.ts = take(sizeof(double) * RC);
-  L.targ = take(sizeof(int) * RC);
-  L.dm = take(sizeof(float) * RC);
-  L.ds = take(sizeof(double) * RC);
-  L.darg = take(sizeof(int) * RC);
-  L.dtv = take(sizeof(float) * RC * Fa);
-  L.dti = take(sizeof(int) * RC * Fa);
-  L.ftok = take(sizeof(int) * R * Fa);
-  L.fprob = take(sizeof(float) * R * Fa);
+  L.tm = take(sizeof(float) * RS);
+  L.ts = take(sizeof(double) * RS);
+  L.targ = take(sizeof(int) * RS);
+  L.dm = take(sizeof(float) * RS);
+  L.ds = take(sizeof(double) * RS);
+  L.darg = take(sizeof(int) * RS);
+  L.dtv = take(sizeof(float) * RS * Fa);
+  L.dti = take(sizeof(int) * RS * Fa);
   L.rows = take(sizeof(RowRec) * R);
   L.seqs = take(sizeof(SeqRec) * B);
-  L.kr = take(sizeof(double) * RC * kU);
-  L.kp = take(sizeof(double) * RC * kU);
+  L.ctr = take(sizeof(double) * R * cpr);
+  L.ctp = take(sizeof(double) * R * cpr);
+  L.cnt = take(sizeof(unsigned) * R * kCtrStride);
   L.total = o;
   return L;
 }
@@ -1030,9 +1161,6 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
 static Ws bind_ws(void* base, const Layout& L) {
   uint8_t* p = static_cast<uint8_t*>(base);
   Ws w;
-  w.row_ctr = reinterpret_cast<unsigned*>(p + L.row_ctr);
-  w.seq_ctr = reinterpret_cast<unsigned*>(p + L.seq_ctr);
-  w.k2_ctr = reinterpret_cast<unsigned*>(p + L.k2_ctr);
   w.tm = reinterpret_cast<float*>(p + L.tm);
   w.ts = reinterpret_cast<double*>(p + L.ts);
   w.targ = reinterpret_cast<int*>(p + L.targ);
@@ -1041,26 +1169,24 @@ static Ws bind_ws(void* base, const Layout& L) {
   w.darg = reinterpret_cast<int*>(p + L.darg);
   w.dtv = reinterpret_cast<float*>(p + L.dtv);
   w.dti = reinterpret_cast<int*>(p + L.dti);
-  w.ftok = reinterpret_cast<int*>(p + L.ftok);
-  w.fprob = reinterpret_cast<float*>(p + L.fprob);
   w.rows = reinterpret_cast<RowRec*>(p + L.rows);
   w.seqs = reinterpret_cast<SeqRec*>(p + L.seqs);
-  w.kr = reinterpret_cast<double*>(p + L.kr);
-  w.kp = reinterpret_cast<double*>(p + L.kp);
+  w.ctr = reinterpret_cast<double*>(p + L.ctr);
+  w.ctp = reinterpret_cast<double*>(p + L.ctp);
+  w.cnt = reinterpret_cast<unsigned*>(p + L.cnt);
   return w;
 }
 
-// Chunks per row for a dtype.
+static int64_t slabs_per_row(int dtype, int64_t V) {
+  const int64_t s = (dtype == SV_BF16) ? slab_elems<uint16_t>() : slab_elems<float>();
+  return (V + s - 1) / s;
+}
 static int64_t chunks_per_row(int dtype, int64_t V) {
-  const int64_t ch = (dtype == SV_BF16) ? chunk_elems<uint16_t>() : chunk_elems<float>();
-  return (V + ch - 1) / ch;
+  return (slabs_per_row(dtype, V) + kU - 1) / kU;
 }
 
-constexpr int64_t kMaxV = (int64_t)1 << 26;
-
 static size_t workspace_bytes(int64_t R, int64_t B, int64_t V, int f) {
-  const int64_t cpr = chunks_per_row(SV_F32, V);  // fp32 has the smaller chunks
-  return make_layout(R, B, cpr, fork_F(f)).total;
+  return make_layout(R, B, chunks_per_row(SV_F32, V), fork_F(f)).total;
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -1100,29 +1226,43 @@ static Params base_params(const sv_batch* in) {
   P.drafts = in->draft_tokens;
   P.tau = in->temperature;
   P.B = in->B; P.k = in->k; P.V = in->V;
+  P.nslab = (int32_t)slabs_per_row(in->dtype, in->V);
   P.cpr = (int32_t)chunks_per_row(in->dtype, in->V);
   P.rows_per_temp = 1;
   return P;
 }
 
-// Segments: each k_stats wave folds seg_chunks consecutive chunks of one row.
-// The segment size is chosen so that the grid is about one resident round
-// of waves (CUs x 24: six waves per SIMD at the kernel's register use);
-// more chunks per wave amortise the per-wave cross-lane work.
+// Waves of k_stats<In, F> that fit on the device at once (occupancy query,
+// cached per instantiation and device).
+template <typename In, int F>
+static int64_t resident_waves() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)k_stats<In, F>, kBlock,
+                                                   0) != hipSuccess ||
+      blocks <= 0)
+    blocks = 4;
+  v = (int64_t)cus * blocks * kWavesPerBlock;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Segments per row: one resident round of waves, each with an equal share of
+// its row's slabs.
+template <typename In, int F>
 static void plan_segments(Params& P) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-  }
-  const int64_t target = (int64_t)cus * 24;
-  const int64_t chunks = P.nslots * (int64_t)P.cpr;
-  int64_t g = (chunks + target - 1) / target;
-  if (g < 1) g = 1;
-  if (g > P.cpr) g = P.cpr;
-  P.seg_chunks = (int32_t)g;
-  P.nseg = (int32_t)((P.cpr + g - 1) / g);
+  const int64_t res = resident_waves<In, F>();
+  int64_t g = res / std::max<int64_t>(P.nslots, 1);
+  g = std::max<int64_t>(1, std::min<int64_t>(g, std::min<int64_t>(kMaxSeg, P.nslab)));
+  P.nseg = (int32_t)g;
+  P.nparts = (int32_t)g;
 }
 
 static dim3 grid_for(int64_t waves) {
@@ -1130,28 +1270,38 @@ static dim3 grid_for(int64_t waves) {
 }
 
 template <typename In, int F>
-static hipError_t launch_stats_F(const Params& P, hipStream_t s) {
+static hipError_t launch_stats_F(Params& P, hipStream_t s) {
+  plan_segments<In, F>(P);
   const int64_t waves = P.nslots * P.nseg;
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL((k_stats<In, F>), grid_for(waves), dim3(kBlock), 0, s, P);
   return hipGetLastError();
 }
 
-template <typename In>
-static hipError_t launch_stats(const Params& P, hipStream_t s) {
-  switch (P.F) {
-    case 0: return launch_stats_F<In, 0>(P, s);
-    case 4: return launch_stats_F<In, 4>(P, s);
-    default: return launch_stats_F<In, 16>(P, s);
-  }
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      v <= 0)
+    v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
-template <typename In>
-static hipError_t launch_resid(const Params& P, hipStream_t s) {
-  const int64_t nslots = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
-  const int64_t waves = nslots * P.cpr;
-  if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_resid<In>), grid_for(waves), dim3(kBlock), 0, s, P);
+// k_decide: enough blocks per task row to cover the device (one 1024-thread
+// block per CU), at least eight chunks of the summed row per block.
+template <typename In, int F>
+static hipError_t launch_decide_F(Params P, hipStream_t s) {
+  const int64_t tasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
+  if (tasks == 0) return hipSuccess;
+  int64_t nbs = device_cus() / tasks;
+  nbs = std::max<int64_t>(1, std::min<int64_t>(nbs, std::max<int64_t>(1, P.cpr / 8)));
+  P.nbs = (int32_t)nbs;
+  hipLaunchKernelGGL((k_decide<In, F>), dim3((unsigned)(tasks * nbs)), dim3(kDecideBlock), 0, s,
+                     P);
   return hipGetLastError();
 }
 
@@ -1164,13 +1314,30 @@ static hipError_t launch_write(const Params& P, hipStream_t s) {
   return hipGetLastError();
 }
 
-static hipError_t dispatch_stats(int dtype, const Params& P0, hipStream_t s) {
-  Params P = P0;
-  plan_segments(P);
+template <typename In>
+static hipError_t launch_stats(Params& P, hipStream_t s) {
+  switch (P.F) {
+    case 0: return launch_stats_F<In, 0>(P, s);
+    case 4: return launch_stats_F<In, 4>(P, s);
+    default: return launch_stats_F<In, 16>(P, s);
+  }
+}
+template <typename In>
+static hipError_t launch_decide(const Params& P, hipStream_t s) {
+  switch (P.F) {
+    case 0: return launch_decide_F<In, 0>(P, s);
+    case 4: return launch_decide_F<In, 4>(P, s);
+    default: return launch_decide_F<In, 16>(P, s);
+  }
+}
+
+// The statistics launch plans the segments into P (k_decide and k_write read
+// P.nseg).
+static hipError_t dispatch_stats(int dtype, Params& P, hipStream_t s) {
   return dtype == SV_BF16 ? launch_stats<uint16_t>(P, s) : launch_stats<float>(P, s);
 }
-static hipError_t dispatch_resid(int dtype, const Params& P, hipStream_t s) {
-  return dtype == SV_BF16 ? launch_resid<uint16_t>(P, s) : launch_resid<float>(P, s);
+static hipError_t dispatch_decide(int dtype, const Params& P, hipStream_t s) {
+  return dtype == SV_BF16 ? launch_decide<uint16_t>(P, s) : launch_decide<float>(P, s);
 }
 static hipError_t dispatch_write(int dtype, const Params& P, hipStream_t s) {
   return dtype == SV_BF16 ? launch_write<uint16_t>(P, s) : launch_write<float>(P, s);
@@ -1216,7 +1383,7 @@ const char* sv_status_string(int32_t s) {
   }
 }
 
-const char* sv_version(void) { return "libspecverify 0.1.0 gfx950"; }
+const char* sv_version(void) { return "libspecverify 0.2.0 gfx950"; }
 
 sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows, int32_t V,
                           int64_t row_stride, const float* temperature, int64_t rows_per_temp,
@@ -1237,6 +1404,7 @@ sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows, int32
   P.T = logits; P.t_row = row_stride; P.t_seq = row_stride;
   P.tau = temperature;
   P.B = (int32_t)std::min<int64_t>(rows, 0x7fffffff); P.k = 0; P.V = V; P.f = 0; P.F = 0;
+  P.nslab = (int32_t)slabs_per_row(dtype, V);
   P.cpr = (int32_t)chunks_per_row(dtype, V);
   P.mode = kSoftmax;
   P.nslots = rows;
@@ -1282,7 +1450,7 @@ sv_status sv_verify_ex(const sv_batch* in, const float* u_accept, const float* u
   if (opts && opts->ev_stats_end) {
     if (hipEventRecord((hipEvent_t)opts->ev_stats_end, s) != hipSuccess) return SV_ERR_HIP;
   }
-  if (dispatch_resid(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
+  if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 
@@ -1317,7 +1485,7 @@ sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,
                                  chunks_per_row(SV_F32, in->V), 0));
   hipStream_t s = (hipStream_t)stream;
   if (dispatch_stats(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
-  if (dispatch_resid(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
+  if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   if (residual && dispatch_write(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
@@ -1339,7 +1507,9 @@ sv_status sv_forked_topf(const sv_batch* in, const sv_forks* forks, void* ws, si
   P.fork_prob = forks->probs;
   P.nslots = (int64_t)in->B * (in->k + 1);
   P.ws = bind_ws(ws, make_layout(P.nslots, in->B, chunks_per_row(SV_F32, in->V), P.F));
-  if (dispatch_stats(in->dtype, P, (hipStream_t)stream) != hipSuccess) return SV_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if (dispatch_stats(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
+  if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

@@ -1,11 +1,11 @@
 // Device-side building blocks of libspecverify (gfx950, wave64).
 //
-// Layout convention used by every kernel: a logits row is cut into chunks of
-// kLanes * kU 16-byte vectors; one wavefront owns one chunk of one row.  Lane
-// l holds vectors u = 0..kU-1 at element offsets (u * 64 + l) * VEC inside
-// the chunk, so each vector load instruction of the wave reads 1 KiB of
-// contiguous memory, and a lane visits its own elements in increasing token
-// id order (u outer, element inner).
+// Layout convention used by every kernel: a logits row is cut into slabs of
+// kLanes 16-byte vectors (512 bf16 or 256 fp32 elements); lane l holds the
+// l-th vector of a slab, so one vector load instruction of a wave reads 1 KiB
+// of contiguous memory.  A wave walks a row kU slabs (a chunk) at a time;
+// inside a chunk lane l's vector u is at element (u * 64 + l) * VEC, so token
+// order inside a chunk is slab by slab (u outer, lanes inner).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,14 +44,14 @@ __device__ __forceinline__ float uniform(float x) {
 }
 
 // ---------------------------------------------------------------- handoffs
-// Hand-off of data between wavefronts of one launch (a chunk's partials to
-// the wave that merges its row; a row's record to the wave that decides the
-// sequence).  The data are written with device-scope stores (sc1: written
-// through to the device-coherent level) and read with device-scope loads;
-// the writer waits for its stores to complete (s_waitcnt vmcnt(0)) before it
-// bumps the counter with a device-scope atomic, and the reader loads only
-// after seeing the final count.  A device-scope fence would also write back
-// the whole L2 of the wave's XCD, once per wave; this avoids that.
+// Hand-off of data between workgroups of one launch (the blocks that share
+// one row's residual sums and the block that draws from them).  The data are
+// written with device-scope stores (sc1: written through to the
+// device-coherent level) and read with device-scope loads; each writer waits
+// for its stores to complete (s_waitcnt vmcnt(0)) before the arrival is
+// counted with a device-scope atomic, and the reader loads only after
+// seeing the final count.  A device-scope fence would also write back the
+// whole L2 of the writer's XCD; this avoids that.
 
 template <typename T>
 __device__ __forceinline__ void st_dev(T* p, T v) {
@@ -65,15 +65,15 @@ __device__ __forceinline__ T ld_dev(const T* p) {
 // Waits until this wave's vector memory operations have completed.
 __device__ __forceinline__ void vm_complete() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt not waited on
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited on
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Publishes this wave's device-scope stores and counts its arrival; returns
-// true on the wave that arrives last (count arrivals in total), which also
-// resets the counter for the next launch.
+// Counts one arrival (lane 0 of the calling wave) on a device-scope counter;
+// returns true, in every lane, on the arrival that completes `count`, which
+// also resets the counter for the next launch.  The caller must have made
+// its data visible first (vm_complete in every wave that wrote).
 __device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned count) {
-  vm_complete();
   unsigned old = 0;
   if ((threadIdx.x & 63) == 0)
     old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -97,7 +97,9 @@ template <> struct Elem<uint16_t> {                  // bf16 bit patterns
 };
 
 template <typename In>
-constexpr int chunk_elems() { return kLanes * kU * Elem<In>::VEC; }
+constexpr int slab_elems() { return kLanes * Elem<In>::VEC; }
+template <typename In>
+constexpr int chunk_elems() { return kU * slab_elems<In>(); }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
@@ -129,42 +131,30 @@ __device__ __forceinline__ void set_neg_inf(uint4& v, int e) {
   }
 }
 
-// Loads this lane's kU vectors of one chunk.  Elements at or beyond V read
-// as -inf; beyond-V memory is never touched (a partial vector is loaded
-// element by element).
+// Loads this lane's kU vectors of one chunk: vector u at element
+// e_base + u * slab_elems (e_base = the chunk's first element + lane * VEC).
+// Vectors u >= nvalid and elements at or beyond V read as -inf; that memory
+// is never touched (a partial vector is loaded element by element).  full:
+// nvalid == kU and the whole chunk lies inside the row.
 template <typename In>
-__device__ __forceinline__ void load_chunk(const In* __restrict__ row, int64_t cstart,
+__device__ __forceinline__ void load_vec(const In* __restrict__ row, int64_t e0, int V, uint4& v);
+
+template <typename In>
+__device__ __forceinline__ void load_chunk(const In* __restrict__ row, int64_t e_base, int nvalid,
                                            int V, bool full, uint4 (&raw)[kU]) {
-  constexpr int VEC = Elem<In>::VEC;
-  const int lane = lane_id();
+  constexpr int64_t SLAB = slab_elems<In>();
   if (full) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const In* p = row + cstart + (int64_t)(u * kLanes + lane) * VEC;
-      raw[u] = *reinterpret_cast<const uint4*>(p);
-    }
+    for (int u = 0; u < kU; ++u)
+      raw[u] = *reinterpret_cast<const uint4*>(row + e_base + u * SLAB);
   } else {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t e0 = cstart + (int64_t)(u * kLanes + lane) * VEC;
-      if (e0 + VEC <= V) {
-        raw[u] = *reinterpret_cast<const uint4*>(row + e0);
+      if (u < nvalid) {
+        load_vec<In>(row, e_base + u * SLAB, V, raw[u]);
       } else {
-        uint4 v = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
-                             Elem<In>::kNegInfWord, Elem<In>::kNegInfWord);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if (e0 + e < V) {
-            if constexpr (sizeof(In) == 4) {
-              set_word(v, e, __float_as_uint(row[e0 + e]));
-            } else {
-              const uint32_t h = row[e0 + e];
-              const uint32_t w = word_of(v, e >> 1);
-              set_word(v, e >> 1, (e & 1) ? ((w & 0xffffu) | (h << 16)) : ((w & 0xffff0000u) | h));
-            }
-          }
-        }
-        raw[u] = v;
+        raw[u] = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
+                            Elem<In>::kNegInfWord, Elem<In>::kNegInfWord);
       }
     }
   }
