@@ -79,6 +79,7 @@ struct Ws {
   float* dtv; int* dti;                 // [R * kMaxSeg * F] draft segment top-F
   RowRec* rows;                         // [R]
   SeqRec* seqs;                         // [B]
+  float* xd; float* yd;                 // [R] the drafted token's logits, seen by k_stats
   double* ctr; double* ctp;             // [tasks * cpr] k_decide chunk totals
   unsigned* cnt;                        // [tasks * kCtrStride] k_decide arrivals
 };
@@ -94,8 +95,7 @@ struct Params {
   int32_t B, k, V, f, F, mode, rows_all, want_q;
   int32_t cpr;             // chunks per row
   int32_t nslab;           // slabs per row
-  int32_t nseg;            // k_stats segments per row
-  int32_t nparts;          // partials per row (k_decide, k_write merge this many)
+  int32_t nparts;          // k_stats segments (partials) per row
   int32_t nbs;             // k_decide blocks per task row
   int64_t nslots;          // row slots of k_stats
   int64_t rows_per_temp;   // softmax
@@ -151,7 +151,8 @@ __device__ __forceinline__ float scale_of(float tau) {
 // Which tensors / statistics a row needs.
 struct RowPlan {
   bool pos_ok, readT, readD, topf, greedy, tok;
-  int64_t mask_id;
+  int mask_id;  // element left out of the draft's masked statistics (-1: none)
+  int d_id;     // the drafted token of the row (-1: none)
 };
 
 __device__ __forceinline__ RowPlan plan_row(const Params& P, int b, int j, float tau) {
@@ -168,9 +169,11 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int b, int j, float
   else if (P.mode == kResidual) r.readD = r.pos_ok && j < P.k;
   else r.readD = false;
   r.mask_id = -1;
-  if (r.topf && j < P.k) {
+  r.d_id = -1;
+  if (r.pos_ok && j < P.k && P.mode != kSoftmax) {
     const int d = P.drafts[(int64_t)b * P.k + j];
-    r.mask_id = d;  // out-of-range ids match no element
+    r.d_id = d;  // out-of-range ids match no element
+    if (r.topf) r.mask_id = d;
   }
   return r;
 }
@@ -185,8 +188,8 @@ struct Vec4 {
 };
 
 template <typename In>
-__device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 v3,
-                                            int64_t e_base, int64_t mask_id) {
+__device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 v3, int e_base,
+                                            int mask_id) {
   constexpr int VEC = Elem<In>::VEC;
   static_assert(kU == 4, "mask_token takes four vectors");
   Vec4<In> r;
@@ -195,44 +198,75 @@ __device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 
   for (int u = 0; u < kU; ++u) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      if (e_base + (int64_t)u * slab_elems<In>() + e == mask_id) set_neg_inf<In>(r.v[u], e);
+      if (e_base + u * slab_elems<In>() + e == mask_id) set_neg_inf<In>(r.v[u], e);
     }
   }
   return r;
 }
 
-struct SegState {
+// The value of element `id` if this lane holds it in the chunk (else -inf),
+// and whether it does.
+template <typename In>
+__device__ __noinline__ float2 pick_elem(uint4 v0, uint4 v1, uint4 v2, uint4 v3, int e_base,
+                                         int id) {
+  constexpr int VEC = Elem<In>::VEC;
+  static_assert(kU == 4, "pick_elem takes four vectors");
+  const uint4 raw[kU] = {v0, v1, v2, v3};
+  float x = neg_inf(), found = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (e_base + u * slab_elems<In>() + e == id) { x = elem<In>(raw[u], e); found = 1.0f; }
+    }
+  }
+  return make_float2(x, found);
+}
+
+struct WaveState {
   Warm tw, dw;    // temperature > 0
   Greedy tg, dg;  // temperature 0
   int nc;         // fork candidate slots in use (this lane)
   float kv;       // fork candidate threshold (wave-uniform)
 };
 
+// Writes element id of a chunk (held by one lane, if any) to *out.
+template <typename In>
+__device__ __forceinline__ void capture(const uint4 (&raw)[kU], int e_base, int id, float* out) {
+  const float2 r = pick_elem<In>(raw[0], raw[1], raw[2], raw[3], e_base, id);
+  if (r.y != 0.0f) *out = r.x;
+}
+
 // One chunk of a segment, already in registers.  RT / RD: the target / draft
 // row is read; GREEDY: temperature 0; FIRST: the segment's first chunk.
 // cs: the chunk's first element (wave-uniform); e_base = cs + lane * VEC;
 // nv: vectors of the chunk inside the segment (the others read as -inf).
+// The drafted token's logits are written to xd / yd when the chunk holds it.
 template <typename In, int F, bool RT, bool RD, bool GREEDY, bool FIRST>
 __device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* drow,
                                             const uint4 (&traw)[kU], uint4 (&draw)[kU],
-                                            int64_t cs, int64_t e_base, int nv, float c,
-                                            SegState& st, CandLds<F>* L) {
-  constexpr int64_t SLAB = slab_elems<In>();
-  constexpr int64_t CH = chunk_elems<In>();
+                                            int cs, int e_base, int nv, float c, WaveState& st,
+                                            CandLds<F>* L, float* xd, float* yd) {
+  constexpr int SLAB = slab_elems<In>();
+  constexpr int CH = chunk_elems<In>();
+  // only vectors [0, nv) of the chunk belong to this segment
+  const bool has_d = pl.d_id >= cs && pl.d_id < cs + nv * SLAB;
   if constexpr (RT) {
-    float vs[kU], m8[kU];
+    if (has_d) capture<In>(traw, e_base, pl.d_id, xd);
+    float m8[kU];
     if constexpr (GREEDY) greedy_fold<In>(st.tg, traw, e_base, true, m8);
-    else warm_fold<In, FIRST>(st.tw, traw, c, vs, m8);
+    else warm_fold<In, FIRST>(st.tw, traw, c, m8);
   }
   if constexpr (RD) {
+    if (has_d) capture<In>(draw, e_base, pl.d_id, yd);
     if (pl.mask_id >= cs && pl.mask_id < cs + CH) {
       const Vec4<In> m = mask_token<In>(draw[0], draw[1], draw[2], draw[3], e_base, pl.mask_id);
 #pragma unroll
       for (int u = 0; u < kU; ++u) draw[u] = m.v[u];
     }
-    float vs[kU], m8[kU];
+    float m8[kU], vs[kU];
     if constexpr (GREEDY) greedy_fold<In>(st.dg, draw, e_base, !pl.topf, m8);
-    else warm_fold<In, FIRST>(st.dw, draw, c, vs, m8);
+    else warm_fold_vs<In, FIRST>(st.dw, draw, c, m8, vs);
     if constexpr (F > 0) {
       if (pl.topf) {
         unsigned bits = 0;
@@ -273,33 +307,34 @@ __device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* 
 // next chunk's loads are issued before the current chunk is folded.
 template <typename In, int F, bool RT, bool RD, bool GREEDY>
 __device__ __forceinline__ void stats_segment(const RowPlan& pl, int V, const In* trow,
-                                              const In* drow, int64_t s0, int64_t s1, float c,
-                                              SegState& st, CandLds<F>* L) {
-  constexpr int64_t SLAB = slab_elems<In>();
+                                              const In* drow, int s0, int s1, float c,
+                                              WaveState& st, CandLds<F>* L, float* xd,
+                                              float* yd) {
+  constexpr int SLAB = slab_elems<In>();
   constexpr int VEC = Elem<In>::VEC;
   const int lane = lane_id();
-  const int64_t nch = (s1 - s0 + kU - 1) / kU;
-  const int64_t slim = min(s1, (int64_t)V / SLAB);  // slabs [.., slim) lie inside the row
+  const int nch = (s1 - s0 + kU - 1) / kU;
+  const int slim = min(s1, V / SLAB);  // slabs [.., slim) lie inside the row
   uint4 ta[kU], da[kU], tb[kU], db[kU];
-  auto load = [&](uint4 (&t)[kU], uint4 (&d)[kU], int64_t i) {
-    const int64_t sl = s0 + i * kU;
-    const int nv = (int)min<int64_t>(kU, s1 - sl);
+  auto load = [&](uint4 (&t)[kU], uint4 (&d)[kU], int i) {
+    const int sl = s0 + i * kU;
+    const int nv = min(kU, s1 - sl);
     const bool full = sl + kU <= slim;
-    const int64_t eb = sl * SLAB + lane * VEC;
+    const int eb = sl * SLAB + lane * VEC;
     if constexpr (RT) load_chunk<In>(trow, eb, nv, V, full, t);
     if constexpr (RD) load_chunk<In>(drow, eb, nv, V, full, d);
   };
-  auto fold = [&](const uint4 (&t)[kU], uint4 (&d)[kU], int64_t i, auto first) {
-    const int64_t sl = s0 + i * kU;
-    const int nv = (int)min<int64_t>(kU, s1 - sl);
+  auto fold = [&](const uint4 (&t)[kU], uint4 (&d)[kU], int i, auto first) {
+    const int sl = s0 + i * kU;
+    const int nv = min(kU, s1 - sl);
     stats_chunk<In, F, RT, RD, GREEDY, decltype(first)::value>(pl, V, drow, t, d, sl * SLAB,
                                                                sl * SLAB + lane * VEC, nv, c,
-                                                               st, L);
+                                                               st, L, xd, yd);
   };
   load(ta, da, 0);
   if (nch > 1) load(tb, db, 1);
   fold(ta, da, 0, std::true_type{});
-  for (int64_t i = 1; i < nch; i += 2) {
+  for (int i = 1; i < nch; i += 2) {
     if (i + 1 < nch) load(ta, da, i + 1);
     fold(tb, db, i, std::false_type{});
     if (i + 1 >= nch) break;
@@ -308,19 +343,23 @@ __device__ __forceinline__ void stats_segment(const RowPlan& pl, int V, const In
   }
 }
 
-// Four resident waves per SIMD: enough bytes in flight with the one-chunk
-// prefetch, and the register budget (128) the folding code needs.
+// Four resident waves per SIMD: the register budget (128) the folding code
+// needs, and enough bytes in flight with the one-chunk prefetch.
 #ifndef SV_STATS_WAVES_PER_EU
 #define SV_STATS_WAVES_PER_EU 4
 #endif
 
+// One wave per (row slot, segment): segment g of a row covers slabs
+// [g * nslab / nseg, (g + 1) * nslab / nseg).  The grid is one resident
+// round of waves.
 template <typename In, int F>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params P) {
+  __shared__ CandLds<F> s_cand[kWavesPerBlock];
   const int64_t task = wave_global_id();
-  if (task >= P.nslots * P.nseg) return;
-  const int64_t slot = task / P.nseg;
-  const int seg = (int)(task - slot * P.nseg);
+  if (task >= P.nslots * P.nparts) return;
+  const int64_t slot = task / P.nparts;
+  const int seg = (int)(task - slot * P.nparts);
   int b, j;
   slot_to_bj(P, slot, b, j);
   b = uniform(b);
@@ -330,14 +369,13 @@ __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params 
   const float c = pl.greedy ? 0.0f : scale_of(tau);
   const int lane = lane_id();
   const Ws& W = P.ws;
-  const int64_t s0 = (int64_t)seg * P.nslab / P.nseg;
-  const int64_t s1 = (int64_t)(seg + 1) * P.nslab / P.nseg;
+  const int s0 = (int)((int64_t)seg * P.nslab / P.nparts);
+  const int s1 = (int)((int64_t)(seg + 1) * P.nslab / P.nparts);
   const In* trow = pl.readT ? trow_ptr<In>(P, b, j) : nullptr;
   const In* drow = pl.readD ? drow_ptr<In>(P, b, j) : nullptr;
 
-  __shared__ CandLds<F> s_cand[kWavesPerBlock];
   CandLds<F>* L = &s_cand[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
-  SegState st;
+  WaveState st;
   warm_init(st.tw); warm_init(st.dw);
   greedy_init(st.tg); greedy_init(st.dg);
   st.nc = 0;
@@ -348,31 +386,33 @@ __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params 
       for (int r = 0; r < F; ++r) { L->wv[r] = neg_inf(); L->wi[r] = kEmptyId; }
     }
   }
+  float* xd = W.xd + slot;
+  float* yd = W.yd + slot;
   if (s1 > s0) {
     const int V = P.V;
     if (pl.readT && pl.readD) {
-      if (pl.greedy) stats_segment<In, F, true, true, true>(pl, V, trow, drow, s0, s1, c, st, L);
-      else stats_segment<In, F, true, true, false>(pl, V, trow, drow, s0, s1, c, st, L);
+      if (pl.greedy) stats_segment<In, F, true, true, true>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
+      else stats_segment<In, F, true, true, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
     } else if (pl.readT) {
-      if (pl.greedy) stats_segment<In, F, true, false, true>(pl, V, trow, drow, s0, s1, c, st, L);
-      else stats_segment<In, F, true, false, false>(pl, V, trow, drow, s0, s1, c, st, L);
+      if (pl.greedy) stats_segment<In, F, true, false, true>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
+      else stats_segment<In, F, true, false, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
     } else if (pl.readD) {
-      if (pl.greedy) stats_segment<In, F, false, true, true>(pl, V, trow, drow, s0, s1, c, st, L);
-      else stats_segment<In, F, false, true, false>(pl, V, trow, drow, s0, s1, c, st, L);
+      if (pl.greedy) stats_segment<In, F, false, true, true>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
+      else stats_segment<In, F, false, true, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
     }
   }
   if constexpr (F > 0) {
-    if (pl.topf && pl.readD) cand_reduce<In, F, kCandSlots>(L, drow, P.V, pl.mask_id, st.nc, st.kv);
+    if (pl.topf && pl.readD) cand_reduce<In, F, 8>(L, drow, P.V, pl.mask_id, st.nc, st.kv);
   }
 
   const int64_t part = slot * kMaxSeg + seg;
   if (pl.readT) {
-    const WaveStats w = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
-    if (lane == 0) { W.tm[part] = w.m; W.ts[part] = w.s; W.targ[part] = w.arg; }
+    const WaveStats ws = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
+    if (lane == 0) { W.tm[part] = ws.m; W.ts[part] = ws.s; W.targ[part] = ws.arg; }
   }
   if (pl.readD) {
-    const WaveStats w = pl.greedy ? wave_finish_greedy(st.dg) : wave_finish_warm(st.dw, c);
-    if (lane == 0) { W.dm[part] = w.m; W.ds[part] = w.s; W.darg[part] = w.arg; }
+    const WaveStats ws = pl.greedy ? wave_finish_greedy(st.dg) : wave_finish_warm(st.dw, c);
+    if (lane == 0) { W.dm[part] = ws.m; W.ds[part] = ws.s; W.darg[part] = ws.arg; }
     if constexpr (F > 0) {
       if (pl.topf && lane < F) {
         W.dtv[part * F + lane] = L->wv[lane];
@@ -442,26 +482,19 @@ struct RowStat {
 };
 
 // Merges the partials of row (b, j) into rs (written by lanes 0..f-1 and
-// lane 0).  One wave; every load is issued before the first is used.
+// lane 0).  One wave; every load is issued before the first is used (the
+// partials, the fork lists and the drafted token's logits as seen by
+// k_stats are loaded whether or not the row needs them).
 template <typename In, int F>
 __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float tau, RowStat* rs) {
   const int lane = lane_id();
-  const RowPlan pl = plan_row(P, b, j, tau);
-  const float c = pl.greedy ? 0.0f : scale_of(tau);
-  const double cd = (double)c;
   const Ws& W = P.ws;
   const int k = P.k;
   const int np = P.nparts;
-  const int64_t base = slot_of(P, b, j) * kMaxSeg;
+  const int64_t slot = slot_of(P, b, j);
+  const int64_t base = slot * kMaxSeg;
   const float nan = __uint_as_float(0x7fc00000u);
 
-  int d = -1;
-  bool d_ok = false;
-  if (P.mode != kSoftmax && pl.pos_ok && j < k) {
-    d = P.drafts[(int64_t)b * k + j];
-    d_ok = (d >= 0 && d < P.V);
-  }
-  // loads: partials (lane i < np: partial i), fork lists, x_d and y_d
   float tmi = neg_inf(), dmi = neg_inf();
   double tsi = 0.0, dsi = 0.0;
   int tai = kEmptyId, dai = kEmptyId;
@@ -471,22 +504,22 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
   for (int r = 0; r < (F > 0 ? F : 1); ++r) { lv[r] = neg_inf(); li[r] = kEmptyId; }
   if (lane < np) {
     const int64_t e = base + lane;
-    if (pl.readT) { tmi = W.tm[e]; tsi = W.ts[e]; tai = W.targ[e]; }
-    if (pl.readD) {
-      dmi = W.dm[e]; dsi = W.ds[e]; dai = W.darg[e];
-      if constexpr (F > 0) {
-        if (pl.topf) {
+    tmi = W.tm[e]; tsi = W.ts[e]; tai = W.targ[e];
+    dmi = W.dm[e]; dsi = W.ds[e]; dai = W.darg[e];
+    if constexpr (F > 0) {
 #pragma unroll
-          for (int r = 0; r < F; ++r) { lv[r] = W.dtv[e * F + r]; li[r] = W.dti[e * F + r]; }
-        }
-      }
+      for (int r = 0; r < F; ++r) { lv[r] = W.dtv[e * F + r]; li[r] = W.dti[e * F + r]; }
     }
   }
-  float xd = 0.0f, yd = 0.0f;
-  if (d_ok) {
-    if (pl.readT) xd = load_logit<In>(trow_ptr<In>(P, b, j), d);
-    if (pl.readD) yd = load_logit<In>(drow_ptr<In>(P, b, j), d);
-  }
+  const float xd = W.xd[slot], yd = W.yd[slot];
+
+  const RowPlan pl = plan_row(P, b, j, tau);
+  const float c = pl.greedy ? 0.0f : scale_of(tau);
+  const double cd = (double)c;
+  const int d = (int)pl.d_id;
+  const bool d_ok = pl.d_id >= 0 && pl.d_id < P.V;
+  if (!pl.readT) { tmi = neg_inf(); tsi = 0.0; tai = kEmptyId; }
+  if (!pl.readD) { dmi = neg_inf(); dsi = 0.0; dai = kEmptyId; }
 
   float tm = neg_inf(), dm = neg_inf();
   int targ = kEmptyId, darg = kEmptyId;
@@ -796,7 +829,7 @@ __device__ __forceinline__ int resid_draw(const Params& P, const double* tot, co
   // 2. re-read that chunk; vector sums scanned slab by slab
   const int64_t sl = (int64_t)cstar * kU;
   const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
-  const int64_t eb = sl * SLAB + lane * VEC;
+  const int eb = (int)(sl * SLAB) + lane * VEC;
   uint4 t[kU], d[kU];
   load_chunk<In>(trow, eb, nv, P.V, false, t);
   if (kc.has_q) {
@@ -948,7 +981,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
       const int64_t sl = (int64_t)ch * kU;
       const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
       const bool full = sl + kU <= slim;
-      const int64_t eb = sl * SLAB + lane * VEC;
+      const int eb = (int)(sl * SLAB) + lane * VEC;
       load_chunk<In>(trow, eb, nv, P.V, full, t);
       if (has_q) {
         load_chunk<In>(drow, eb, nv, P.V, full, d);
@@ -1061,7 +1094,7 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
   const int64_t sl = (int64_t)chunk * kU;
   const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
   const bool full = sl + kU <= (int64_t)P.V / SLAB;
-  const int64_t eb = sl * SLAB + lane * VEC;
+  const int eb = (int)(sl * SLAB) + lane * VEC;
 
   uint4 traw[kU], draw[kU];
   ResidCoef kc;
@@ -1122,7 +1155,7 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) 
 // ================================================================ host side
 
 struct Layout {
-  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, ctr, ctp, cnt, total;
+  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, ctr, ctp, cnt, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1151,6 +1184,8 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   L.dti = take(sizeof(int) * RS * Fa);
   L.rows = take(sizeof(RowRec) * R);
   L.seqs = take(sizeof(SeqRec) * B);
+  L.xd = take(sizeof(float) * R);
+  L.yd = take(sizeof(float) * R);
   L.ctr = take(sizeof(double) * R * cpr);
   L.ctp = take(sizeof(double) * R * cpr);
   L.cnt = take(sizeof(unsigned) * R * kCtrStride);
@@ -1171,6 +1206,8 @@ static Ws bind_ws(void* base, const Layout& L) {
   w.dti = reinterpret_cast<int*>(p + L.dti);
   w.rows = reinterpret_cast<RowRec*>(p + L.rows);
   w.seqs = reinterpret_cast<SeqRec*>(p + L.seqs);
+  w.xd = reinterpret_cast<float*>(p + L.xd);
+  w.yd = reinterpret_cast<float*>(p + L.yd);
   w.ctr = reinterpret_cast<double*>(p + L.ctr);
   w.ctp = reinterpret_cast<double*>(p + L.ctp);
   w.cnt = reinterpret_cast<unsigned*>(p + L.cnt);
@@ -1232,50 +1269,8 @@ static Params base_params(const sv_batch* in) {
   return P;
 }
 
-// Waves of k_stats<In, F> that fit on the device at once (occupancy query,
-// cached per instantiation and device).
-template <typename In, int F>
-static int64_t resident_waves() {
-  static std::atomic<int64_t> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int64_t v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int cus = 0, blocks = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)k_stats<In, F>, kBlock,
-                                                   0) != hipSuccess ||
-      blocks <= 0)
-    blocks = 4;
-  v = (int64_t)cus * blocks * kWavesPerBlock;
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
-
-// Segments per row: one resident round of waves, each with an equal share of
-// its row's slabs.
-template <typename In, int F>
-static void plan_segments(Params& P) {
-  const int64_t res = resident_waves<In, F>();
-  int64_t g = res / std::max<int64_t>(P.nslots, 1);
-  g = std::max<int64_t>(1, std::min<int64_t>(g, std::min<int64_t>(kMaxSeg, P.nslab)));
-  P.nseg = (int32_t)g;
-  P.nparts = (int32_t)g;
-}
-
 static dim3 grid_for(int64_t waves) {
   return dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
-}
-
-template <typename In, int F>
-static hipError_t launch_stats_F(Params& P, hipStream_t s) {
-  plan_segments<In, F>(P);
-  const int64_t waves = P.nslots * P.nseg;
-  if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_stats<In, F>), grid_for(waves), dim3(kBlock), 0, s, P);
-  return hipGetLastError();
 }
 
 static int device_cus() {
@@ -1289,6 +1284,44 @@ static int device_cus() {
     v = 256;
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
+}
+
+// Waves of k_stats<In, F> that fit on the device at once (occupancy query,
+// cached per instantiation and device).
+template <typename In, int F>
+static int64_t resident_waves() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)k_stats<In, F>, kBlock,
+                                                   0) != hipSuccess ||
+      blocks <= 0)
+    blocks = 4;
+  v = (int64_t)device_cus() * blocks * kWavesPerBlock;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Segments per row: one resident round of waves, each with an equal share
+// of its row's slabs (at most 64 partials per row).
+template <typename In, int F>
+static void plan_segments(Params& P) {
+  const int64_t res = resident_waves<In, F>();
+  int64_t g = res / std::max<int64_t>(P.nslots, 1);
+  g = std::max<int64_t>(1, std::min<int64_t>(g, std::min<int64_t>(kMaxSeg, P.nslab)));
+  P.nparts = (int32_t)g;
+}
+
+template <typename In, int F>
+static hipError_t launch_stats_F(Params& P, hipStream_t s) {
+  plan_segments<In, F>(P);
+  const int64_t waves = P.nslots * P.nparts;
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_stats<In, F>), grid_for(waves), dim3(kBlock), 0, s, P);
+  return hipGetLastError();
 }
 
 // k_decide: enough blocks per task row to cover the device (one 1024-thread
@@ -1331,8 +1364,8 @@ static hipError_t launch_decide(const Params& P, hipStream_t s) {
   }
 }
 
-// The statistics launch plans the segments into P (k_decide and k_write read
-// P.nseg).
+// The statistics launch plans its blocks into P (k_decide and k_write read
+// P.nparts).
 static hipError_t dispatch_stats(int dtype, Params& P, hipStream_t s) {
   return dtype == SV_BF16 ? launch_stats<uint16_t>(P, s) : launch_stats<float>(P, s);
 }

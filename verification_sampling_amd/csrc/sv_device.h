@@ -137,12 +137,12 @@ __device__ __forceinline__ void set_neg_inf(uint4& v, int e) {
 // is never touched (a partial vector is loaded element by element).  full:
 // nvalid == kU and the whole chunk lies inside the row.
 template <typename In>
-__device__ __forceinline__ void load_vec(const In* __restrict__ row, int64_t e0, int V, uint4& v);
+__device__ __forceinline__ void load_vec(const In* __restrict__ row, int e0, int V, uint4& v);
 
 template <typename In>
-__device__ __forceinline__ void load_chunk(const In* __restrict__ row, int64_t e_base, int nvalid,
+__device__ __forceinline__ void load_chunk(const In* __restrict__ row, int e_base, int nvalid,
                                            int V, bool full, uint4 (&raw)[kU]) {
-  constexpr int64_t SLAB = slab_elems<In>();
+  constexpr int SLAB = slab_elems<In>();
   if (full) {
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -163,7 +163,7 @@ __device__ __forceinline__ void load_chunk(const In* __restrict__ row, int64_t e
 // Loads one 16-byte vector at element e0 of a row; elements at or beyond V
 // read as -inf and are never touched.
 template <typename In>
-__device__ __forceinline__ void load_vec(const In* __restrict__ row, int64_t e0, int V, uint4& v) {
+__device__ __forceinline__ void load_vec(const In* __restrict__ row, int e0, int V, uint4& v) {
   constexpr int VEC = Elem<In>::VEC;
   if (e0 + VEC <= V) {
     v = *reinterpret_cast<const uint4*>(row + e0);

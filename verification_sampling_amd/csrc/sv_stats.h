@@ -75,6 +75,9 @@ __device__ __forceinline__ float exp_sums(const uint4 (&raw)[kU], float c, float
       for (int e = 0; e < w; ++e) t[e] = t[e] + t[e + w];
     }
     vs[u] = t[0];
+#ifdef SV_EXP_SCHED
+    __builtin_amdgcn_sched_barrier(0);
+#endif
   }
   float a[kU];
 #pragma unroll
@@ -121,13 +124,13 @@ __device__ __noinline__ WarmFix warm_redo(uint4 v0, uint4 v1, uint4 v2, uint4 v3
   return w;
 }
 
-// Folds one chunk into the lane's sum; vs gets the per-vector sums.  On the
-// segment's first chunk the reference is first set to the lane's maximum of
-// that chunk (m8 then holds the vector maxima).  Every lane must call it (it
-// contains a wave-uniform branch).
+// Folds one chunk into the lane's sum and returns the chunk's sum of terms;
+// vs gets the per-vector sums.  On the segment's first chunk the reference
+// is first set to the lane's maximum of that chunk (m8 then holds the vector
+// maxima).  Every lane must call it (it contains a wave-uniform branch).
 template <typename In, bool FIRST>
-__device__ __forceinline__ void warm_fold(Warm& a, const uint4 (&raw)[kU], float c,
-                                          float (&vs)[kU], float (&m8)[kU]) {
+__device__ __forceinline__ float warm_fold_vs(Warm& a, const uint4 (&raw)[kU], float c,
+                                              float (&m8)[kU], float (&vs)[kU]) {
   if constexpr (FIRST) {
     const float mc = vec_maxima<In>(raw, m8);
     if (mc > neg_inf()) {
@@ -149,12 +152,20 @@ __device__ __forceinline__ void warm_fold(Warm& a, const uint4 (&raw)[kU], float
     }
   }
   a.s += (double)sc;
+  return sc;
+}
+
+template <typename In, bool FIRST>
+__device__ __forceinline__ float warm_fold(Warm& a, const uint4 (&raw)[kU], float c,
+                                           float (&m8)[kU]) {
+  float vs[kU];
+  return warm_fold_vs<In, FIRST>(a, raw, c, m8, vs);
 }
 
 // Temperature 0: running maximum, and the lowest id holding it.  e_base is
 // the element index of the lane's vector 0; vector u starts u slabs later.
 template <typename In>
-__device__ __forceinline__ void greedy_fold(Greedy& a, const uint4 (&raw)[kU], int64_t e_base,
+__device__ __forceinline__ void greedy_fold(Greedy& a, const uint4 (&raw)[kU], int e_base,
                                             bool want_arg, float (&m8)[kU]) {
   constexpr int VEC = Elem<In>::VEC;
   const float mc = vec_maxima<In>(raw, m8);
@@ -166,7 +177,7 @@ __device__ __forceinline__ void greedy_fold(Greedy& a, const uint4 (&raw)[kU], i
     for (int u = 0; u < kU; ++u) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const int id = (int)(e_base + (int64_t)u * slab_elems<In>() + e);
+        const int id = e_base + u * slab_elems<In>() + e;
         if (first == kEmptyId && elem<In>(raw[u], e) == mc) first = id;
       }
     }
@@ -208,16 +219,18 @@ __device__ __forceinline__ WaveStats wave_finish_greedy(const Greedy& a) {
 }
 
 // ---------------------------------------------------------------- forks
-// Fork candidates of a segment.  A vector is a candidate when it may hold an
-// element at or above the threshold kv (the F-th largest lane maximum of the
-// segment's first chunk, raised as better candidates are found): at
-// temperature > 0 when its sum of terms reaches 2^(kv c - hi) (less a margin
-// for rounding), at temperature 0 when its maximum reaches kv.  A candidate
-// lane appends the vector's element index to its own slots in LDS; no
-// cross-lane work happens while streaming.  The slots are reduced (vectors
-// re-read, elements ranked, the wave's top-F kept and kv raised) when some
-// lane could overflow, and at the end of the segment.
-constexpr int kCandSlots = 8;
+// Fork candidates of a wave's segment of a row.  A vector is a candidate
+// when it may hold an element at or above the threshold kv (the F-th
+// largest lane maximum of the segment's first chunk, raised as better
+// candidates are found): at temperature > 0 when its sum of terms reaches
+// 2^(kv c - hi) (less a margin for rounding), at temperature 0 when its
+// maximum reaches kv.  A candidate lane appends the vector's element index
+// to its own slots in LDS; nothing else happens while streaming, so the
+// chunk's registers are free as soon as it is folded.  The slots are
+// reduced (vectors re-read, elements ranked, the wave's top-F kept and kv
+// raised) at the end of the segment, or earlier if some lane could overflow
+// with the next chunk.
+constexpr int kCandSlots = 24;
 
 template <int F>
 struct CandLds {
@@ -226,36 +239,27 @@ struct CandLds {
   int wi[F > 0 ? F : 1];
 };
 
-template <int F>
-__device__ __forceinline__ void cand_reset(CandLds<F>* L) {
-  if constexpr (F > 0) {
-    if (lane_id() < F) { L->wv[lane_id()] = neg_inf(); L->wi[lane_id()] = kEmptyId; }
-  }
-}
-
 // Appends vector u of this lane's chunk when bit u of `bits` is set.
 template <int F>
-__device__ __forceinline__ void cand_append(CandLds<F>* L, unsigned bits, int64_t e_base,
-                                            int64_t slab, int& nc) {
+__device__ __forceinline__ void cand_append(CandLds<F>* L, unsigned bits, int e_base, int slab,
+                                            int& nc) {
   const int lane = lane_id();
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     if ((bits >> u) & 1u) {
-      L->pos[nc][lane] = (int)(e_base + (int64_t)u * slab);
+      L->pos[nc][lane] = e_base + u * slab;
       ++nc;
     }
   }
 }
 
-// Reduces the slots: re-reads the candidate vectors, ranks their elements
-// (id < V, id != mask_id, x >= kv) together with the wave's list, keeps the
-// top-F and raises kv to the F-th once the list is full.  Clears the slots.
-// NB vectors are loaded per round: all slots at the end of a segment (one
-// memory round trip), a few while streaming (the rare overflow path runs
-// with the next chunk's registers live).
+// Reduces the slots: re-reads the candidate vectors (NB per round), ranks
+// their elements (id < V, id != mask_id, at or above the lane's running
+// threshold) together with the wave's list, keeps the top-F and raises kv to
+// the F-th once the list is full.  Clears the slots.
 template <typename In, int F, int NB>
 __device__ __forceinline__ void cand_reduce(CandLds<F>* L, const In* __restrict__ row, int V,
-                                            int64_t mask_id, int& nc, float& kv) {
+                                            int mask_id, int& nc, float& kv) {
   if constexpr (F > 0) {
     constexpr int VEC = Elem<In>::VEC;
     const int lane = lane_id();
@@ -271,23 +275,24 @@ __device__ __forceinline__ void cand_reduce(CandLds<F>* L, const In* __restrict_
       int e0[NB];
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
-        const int i = i0 + q;
         e0[q] = -1;
         v[q] = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
                           Elem<In>::kNegInfWord);
-        if (i < nc) {
-          e0[q] = L->pos[i][lane];
+        if (i0 + q < nc) {
+          e0[q] = L->pos[i0 + q][lane];
           load_vec<In>(row, e0[q], V, v[q]);
         }
       }
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
-        if (e0[q] >= 0) {
+        float thr = fmaxf(kv, mine.v[F - 1]);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float x = elem<In>(v[q], e);
-            const int64_t id = (int64_t)e0[q] + e;
-            if (id < V && id != mask_id && x >= kv) mine.insert(x, (int)id);
+        for (int e = 0; e < VEC; ++e) {
+          const float x = elem<In>(v[q], e);
+          const int id = e0[q] + e;
+          if (x >= thr && e0[q] >= 0 && id < V && id != mask_id) {
+            mine.insert(x, id);
+            thr = fmaxf(kv, mine.v[F - 1]);
           }
         }
       }
