@@ -51,6 +51,7 @@ enum Mode : int { kVerify = 0, kForks = 1, kResidual = 2, kSoftmax = 3 };
 constexpr int kMaxChunks = 1024;
 constexpr int64_t kMaxV = (int64_t)kMaxChunks * kU * kLanes * 4;
 constexpr int kMaxSeg = 64;  // partials per row (one lane each when merged)
+constexpr int kDumpCap = 128;  // fork candidate vectors a k_stats wave passes on
 
 // Arrival counters sit 256 bytes apart: device-scope atomics to one memory
 // line are serialised.
@@ -80,6 +81,7 @@ struct Ws {
   RowRec* rows;                         // [R]
   SeqRec* seqs;                         // [B]
   float* xd; float* yd;                 // [R] the drafted token's logits, seen by k_stats
+  int* cn; int* cpos;                   // [R * kMaxSeg], [R * kMaxSeg * kDumpCap] fork candidates
   double* ctr; double* ctp;             // [tasks * cpr] k_decide chunk totals
   unsigned* cnt;                        // [tasks * kCtrStride] k_decide arrivals
 };
@@ -401,11 +403,24 @@ __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params 
       else stats_segment<In, F, false, true, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
     }
   }
+  const int64_t part = slot * kMaxSeg + seg;
   if constexpr (F > 0) {
-    if (pl.topf && pl.readD) cand_reduce<In, F, 8>(L, drow, P.V, pl.mask_id, st.nc, st.kv);
+    if (pl.topf && pl.readD) {
+      // pass the candidate positions on, compacted; rank them here only if
+      // they do not fit
+      int incl = wave_inclusive_scan_i(st.nc);
+      int total = readlane_i(incl, kLanes - 1);
+      if (total > kDumpCap) {
+        cand_reduce<In, F, 8>(L, drow, P.V, pl.mask_id, st.nc, st.kv);
+        incl = 0;
+        total = 0;
+      }
+      int* dst = W.cpos + part * kDumpCap + (incl - st.nc);
+      for (int i = 0; i < st.nc; ++i) dst[i] = L->pos[i][lane];
+      if (lane == 0) W.cn[part] = total;
+    }
   }
 
-  const int64_t part = slot * kMaxSeg + seg;
   if (pl.readT) {
     const WaveStats ws = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
     if (lane == 0) { W.tm[part] = ws.m; W.ts[part] = ws.s; W.targ[part] = ws.arg; }
@@ -471,22 +486,125 @@ __device__ __forceinline__ Merged merge_lanes(float mi, double si, int ai, bool 
   return r;
 }
 
+// The candidate vectors the segments of row (b, j) passed on (cnt: this
+// lane's segment's count, lanes < np): positions, then vectors, are loaded
+// a round of 64 * kRound at a time; their elements (id < V, id != mask_id)
+// at or above the F-th largest of the lanes' maxima over the loaded
+// vectors go into this lane's list.  That bound never drops one of the
+// row's top-F: at least F of the loaded elements reach it.
+template <typename In, int F>
+__device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, int64_t base,
+                                                int np, int cnt, int mask_id, TopList<F>& mine) {
+  if constexpr (F > 0) {
+    constexpr int VEC = Elem<In>::VEC;
+    constexpr int kRound = 4;
+    const int lane = lane_id();
+    const int mycnt = lane < np ? cnt : 0;
+    const int incl = wave_inclusive_scan_i(mycnt);
+    const int total = readlane_i(incl, kLanes - 1);
+    const In* drow = drow_ptr<In>(P, b, j);
+    const int V = P.V;
+    for (int t0 = 0; t0 < total; t0 += kLanes * kRound) {
+      int pos[kRound];
+#pragma unroll
+      for (int q = 0; q < kRound; ++q) {
+        const int t = t0 + q * kLanes + lane;
+        // segment holding flat index t; the lane reads happen with every
+        // lane active (a cross-lane read from an inactive lane returns 0)
+        int seg = 0;
+        for (int g = 0; g < np; ++g) seg += (readlane_i(incl, g) <= t) ? 1 : 0;
+        seg = min(seg, np - 1);
+        const int before = __shfl(incl, seg) - __shfl(mycnt, seg);
+        pos[q] = -1;
+        if (t < total) pos[q] = P.ws.cpos[(base + seg) * kDumpCap + (t - before)];
+      }
+      uint4 v[kRound];
+#pragma unroll
+      for (int q = 0; q < kRound; ++q) {
+        v[q] = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
+                          Elem<In>::kNegInfWord);
+        if (pos[q] >= 0) load_vec<In>(drow, pos[q], V, v[q]);
+      }
+      float lm = neg_inf();
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < kRound; ++q) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int id = pos[q] + e;
+          if (pos[q] >= 0 && id < V && id != mask_id) { lm = fmaxf(lm, elem<In>(v[q], e)); any = true; }
+        }
+      }
+      // a lane with an element at -inf still counts towards the F
+      const float key = any ? lm : neg_inf();
+      const unsigned long long have = __ballot(any);
+      const float kvr = (__popcll(have) >= F) ? wave_fth_largest<F>(key, F) : neg_inf();
+#pragma unroll
+      for (int q = 0; q < kRound; ++q) {
+        float thr = fmaxf(kvr, mine.v[F - 1]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float x = elem<In>(v[q], e);
+          const int id = pos[q] + e;
+          if (pos[q] >= 0 && id < V && id != mask_id && x >= thr) {
+            mine.insert(x, id);
+            thr = fmaxf(kvr, mine.v[F - 1]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // A row's merged statistics (LDS, one per row of the sequence).
 struct RowStat {
   float tm; int targ; double ts;   // target reference, argmax, sum
   float dm; int darg; double ds;   // draft (unmasked row)
+  float qm; double qs;             // draft with the drafted token masked (forks)
   double pd, qd;                   // p(d), q(d) for j < k
   int valid;
   int ftok[kMaxF];                 // forks (f entries)
   float fprob[kMaxF];
 };
 
+// The row's forks: the top-f of the segments' lists and of the candidate
+// vectors they passed on, with masked-softmax probabilities at tau
+// (2^((v - m') c) / S', (1, 0, ...) at temperature 0); lane r < f gets entry
+// r in (tok, prob).
+template <typename In, int F>
+__device__ __forceinline__ void fork_top(const Params& P, int b, int j, const RowPlan& pl,
+                                         const float (&lv)[F > 0 ? F : 1],
+                                         const int (&li)[F > 0 ? F : 1], int cnt, float qm,
+                                         double qs, double cd, TopList<F>& top, int& tok,
+                                         float& prob) {
+  const int lane = lane_id();
+  tok = kEmptyId;
+  prob = 0.0f;
+  if constexpr (F > 0) {
+    TopList<F> mine;
+    mine.clear();
+#pragma unroll
+    for (int r = 0; r < F; ++r) mine.insert(lv[r], li[r]);
+    fork_candidates<In, F>(P, b, j, slot_of(P, b, j) * kMaxSeg, P.nparts, cnt, pl.mask_id, mine);
+    wave_merge_lists<F>(mine, P.f, top);
+    float v = neg_inf();
+#pragma unroll
+    for (int r = 0; r < F; ++r) {
+      if (lane == r) { v = top.v[r]; tok = top.i[r]; }
+    }
+    if (pl.greedy) prob = (lane == 0) ? 1.0f : 0.0f;
+    else if (!finitef(qm) || !(v > neg_inf())) prob = 0.0f;
+    else prob = (float)(exp2(((double)v - (double)qm) * cd) / qs);
+  }
+}
+
 // Merges the partials of row (b, j) into rs (written by lanes 0..f-1 and
 // lane 0).  One wave; every load is issued before the first is used (the
 // partials, the fork lists and the drafted token's logits as seen by
 // k_stats are loaded whether or not the row needs them).
 template <typename In, int F>
-__device__ __forceinline__ void row_stat(const Params& P, int b, int j, float tau, RowStat* rs) {
+__device__ __forceinline__ void row_stat(const Params& P, int b, int j, float tau, RowStat* rs,
+                                         bool forks_now) {
   const int lane = lane_id();
   const Ws& W = P.ws;
   const int k = P.k;
@@ -502,6 +620,7 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
   int li[F > 0 ? F : 1];
 #pragma unroll
   for (int r = 0; r < (F > 0 ? F : 1); ++r) { lv[r] = neg_inf(); li[r] = kEmptyId; }
+  int cnt = 0;
   if (lane < np) {
     const int64_t e = base + lane;
     tmi = W.tm[e]; tsi = W.ts[e]; tai = W.targ[e];
@@ -509,6 +628,7 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
     if constexpr (F > 0) {
 #pragma unroll
       for (int r = 0; r < F; ++r) { lv[r] = W.dtv[e * F + r]; li[r] = W.dti[e * F + r]; }
+      cnt = W.cn[e];
     }
   }
   const float xd = W.xd[slot], yd = W.yd[slot];
@@ -536,29 +656,14 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
   top.clear();
   if (pl.readD) {
     const Merged q = merge_lanes(dmi, dsi, dai, pl.greedy, cd);
+    if (lane == 0) { rs->qm = q.m; rs->qs = q.s; }
     if (pl.topf) {
       if constexpr (F > 0) {
-        // the segments' lists hold the row's top-f (masked)
-        TopList<F> mine;
-        mine.clear();
-#pragma unroll
-        for (int r = 0; r < F; ++r) mine.insert(lv[r], li[r]);
-        wave_merge_lists<F>(mine, P.f, top);
-        // masked softmax at tau of the selected tokens: 2^((v - m') c) / S',
-        // lane r computes entry r
-        float v = neg_inf();
-        int id = kEmptyId;
-#pragma unroll
-        for (int r = 0; r < F; ++r) {
-          if (lane == r) { v = top.v[r]; id = top.i[r]; }
-        }
-        if (lane < P.f) {
-          float pr;
-          if (pl.greedy) pr = (lane == 0) ? 1.0f : 0.0f;
-          else if (!finitef(q.m) || !(v > neg_inf())) pr = 0.0f;
-          else pr = (float)(exp2(((double)v - (double)q.m) * cd) / q.s);
-          rs->ftok[lane] = id;
-          rs->fprob[lane] = pr;
+        if (forks_now) {
+          int tok;
+          float prob;
+          fork_top<In, F>(P, b, j, pl, lv, li, cnt, q.m, q.s, cd, top, tok, prob);
+          if (lane < P.f) { rs->ftok[lane] = tok; rs->fprob[lane] = prob; }
         }
       }
       if (j < k) {
@@ -909,6 +1014,31 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int K1 = P.k + 1;
+  const int64_t ntasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * K1 : P.B;
+  if ((int64_t)blockIdx.x >= ntasks * P.nbs) {
+    // a fork block: the forks of one sequence at temperature > 0, ranked
+    // beside the blocks that sum and draw
+    const int b = (int)(blockIdx.x - ntasks * P.nbs);
+    const float tau = P.tau[b];
+    if (!(tau > 0.0f && tau_ok(tau))) return;  // the owner block ranks these
+    for (int j = w; j < K1; j += kDecideWaves) row_stat<In, F>(P, b, j, tau, &S.rs[j], true);
+    __syncthreads();
+    if (w == 0) {
+      int n, status;
+      decide_sequence(P, b, S, false, n, status);
+      if (lane == 0) S.status = status;
+    }
+    __syncthreads();
+    if (S.status == 0) return;
+    for (int j = w; j < K1; j += kDecideWaves) {
+      if (lane < P.f) {
+        const int64_t o = ((int64_t)b * K1 + j) * P.f + lane;
+        P.fork_tok[o] = S.rs[j].ftok[lane];
+        if (P.fork_prob) P.fork_prob[o] = S.rs[j].fprob[lane];
+      }
+    }
+    return;
+  }
   const int64_t task = blockIdx.x / P.nbs;
   const int part = (int)(blockIdx.x - task * P.nbs);
   int b, jt;  // sequence, and the task's own row in the full-residual mode
@@ -922,14 +1052,17 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const float tau = P.tau[b];
   const bool owner = jt <= 0 && part == 0;  // writes the per-sequence outputs
 
-  // 1. row statistics, one wave per row
+  // 1. row statistics, one wave per row.  Forks are ranked here by the
+  // owner at temperature 0 (the greedy q(d) needs the draft's top-1) and for
+  // the forks-only call; at temperature > 0 a fork block of their own does.
+  const bool forks_now = owner && (P.mode == kForks || !(tau > 0.0f && tau_ok(tau)));
   if (P.mode == kResidual && !P.rows_all) {
     if (w == 0) {
       const int pos = P.position[b];
-      if (pos >= 0 && pos <= P.k) row_stat<In, F>(P, b, pos, tau, &S.rs[pos]);
+      if (pos >= 0 && pos <= P.k) row_stat<In, F>(P, b, pos, tau, &S.rs[pos], false);
     }
   } else {
-    for (int j = w; j < K1; j += kDecideWaves) row_stat<In, F>(P, b, j, tau, &S.rs[j]);
+    for (int j = w; j < K1; j += kDecideWaves) row_stat<In, F>(P, b, j, tau, &S.rs[j], forks_now);
   }
   __syncthreads();
 
@@ -944,8 +1077,8 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const int n = S.n;
   const int status = S.status;
 
-  // 3. forks
-  if (owner && status != 0 && P.fork_tok) {
+  // 3. forks ranked in step 1
+  if (forks_now && status != 0 && P.fork_tok) {
     for (int j = w; j < K1; j += kDecideWaves) {
       if (lane < P.f) {
         const int64_t o = ((int64_t)b * K1 + j) * P.f + lane;
@@ -1155,7 +1288,7 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) 
 // ================================================================ host side
 
 struct Layout {
-  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, ctr, ctp, cnt, total;
+  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, cn, cpos, ctr, ctp, cnt, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1186,6 +1319,8 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   L.seqs = take(sizeof(SeqRec) * B);
   L.xd = take(sizeof(float) * R);
   L.yd = take(sizeof(float) * R);
+  L.cn = take(F > 0 ? sizeof(int) * RS : 0);
+  L.cpos = take(F > 0 ? sizeof(int) * RS * kDumpCap : 0);
   L.ctr = take(sizeof(double) * R * cpr);
   L.ctp = take(sizeof(double) * R * cpr);
   L.cnt = take(sizeof(unsigned) * R * kCtrStride);
@@ -1207,6 +1342,8 @@ static Ws bind_ws(void* base, const Layout& L) {
   w.rows = reinterpret_cast<RowRec*>(p + L.rows);
   w.seqs = reinterpret_cast<SeqRec*>(p + L.seqs);
   w.xd = reinterpret_cast<float*>(p + L.xd);
+  w.cn = reinterpret_cast<int*>(p + L.cn);
+  w.cpos = reinterpret_cast<int*>(p + L.cpos);
   w.yd = reinterpret_cast<float*>(p + L.yd);
   w.ctr = reinterpret_cast<double*>(p + L.ctr);
   w.ctp = reinterpret_cast<double*>(p + L.ctp);
@@ -1325,16 +1462,18 @@ static hipError_t launch_stats_F(Params& P, hipStream_t s) {
 }
 
 // k_decide: enough blocks per task row to cover the device (one 1024-thread
-// block per CU), at least eight chunks of the summed row per block.
+// block per CU), at least eight chunks of the summed row per block, plus one
+// fork block per sequence when verify asks for forks.
 template <typename In, int F>
 static hipError_t launch_decide_F(Params P, hipStream_t s) {
   const int64_t tasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
   if (tasks == 0) return hipSuccess;
-  int64_t nbs = device_cus() / tasks;
+  const int64_t fork_blocks = (P.mode == kVerify && P.fork_tok) ? P.B : 0;
+  int64_t nbs = (device_cus() - fork_blocks) / tasks;
   nbs = std::max<int64_t>(1, std::min<int64_t>(nbs, std::max<int64_t>(1, P.cpr / 8)));
   P.nbs = (int32_t)nbs;
-  hipLaunchKernelGGL((k_decide<In, F>), dim3((unsigned)(tasks * nbs)), dim3(kDecideBlock), 0, s,
-                     P);
+  hipLaunchKernelGGL((k_decide<In, F>), dim3((unsigned)(tasks * nbs + fork_blocks)),
+                     dim3(kDecideBlock), 0, s, P);
   return hipGetLastError();
 }
 

@@ -261,6 +261,18 @@ __device__ __forceinline__ double wave_inclusive_scan(double x) {
   return x + off;
 }
 
+// The same for integers.
+__device__ __forceinline__ int wave_inclusive_scan_i(int x) {
+  x += dpp_i<kDppRowShr1>(x);
+  x += dpp_i<kDppRowShr2>(x);
+  x += dpp_i<kDppRowShr4>(x);
+  x += dpp_i<kDppRowShr8>(x);
+  const int t0 = readlane_i(x, 15), t1 = readlane_i(x, 31), t2 = readlane_i(x, 47);
+  const int row = lane_id() >> 4;
+  const int off = row == 0 ? 0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+  return x + off;
+}
+
 // Ranking key of fork candidates: higher logit first, lower id on ties.
 // An empty slot is (-inf, kEmptyId): any real element, even at -inf, beats it.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {

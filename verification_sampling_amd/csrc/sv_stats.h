@@ -226,10 +226,12 @@ __device__ __forceinline__ WaveStats wave_finish_greedy(const Greedy& a) {
 // 2^(kv c - hi) (less a margin for rounding), at temperature 0 when its
 // maximum reaches kv.  A candidate lane appends the vector's element index
 // to its own slots in LDS; nothing else happens while streaming, so the
-// chunk's registers are free as soon as it is folded.  The slots are
-// reduced (vectors re-read, elements ranked, the wave's top-F kept and kv
-// raised) at the end of the segment, or earlier if some lane could overflow
-// with the next chunk.
+// chunk's registers are free as soon as it is folded.  At the end of the
+// segment the positions are written out, compacted, for the decide kernel
+// to rank; the slots are reduced in the wave instead (vectors re-read,
+// elements ranked, the wave's top-F kept and kv raised) only if some lane
+// could overflow with the next chunk, or if the segment has more
+// candidates than its share of the output.
 constexpr int kCandSlots = 24;
 
 template <int F>
