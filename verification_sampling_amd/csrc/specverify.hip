@@ -65,8 +65,7 @@ struct RowRec {
   float dm;     // draft reference (unmasked row)
   int valid;
   double ds;    // draft sum of 2^((y - dm) c)
-  double zr;    // residual total sum max(0, p - q)
-  double zp;    // target total sum p
+  double zr;    // total weight: sum of max(0, p - q), or of p at j = k
 };
 
 struct SeqRec {
@@ -82,7 +81,7 @@ struct Ws {
   SeqRec* seqs;                         // [B]
   float* xd; float* yd;                 // [R] the drafted token's logits, seen by k_stats
   int* cn; int* cpos;                   // [R * kMaxSeg], [R * kMaxSeg * kDumpCap] fork candidates
-  double* ctr; double* ctp;             // [tasks * cpr] k_decide chunk totals
+  double* ctr;                          // [tasks * cpr] k_decide chunk totals
   unsigned* cnt;                        // [tasks * kCtrStride] k_decide arrivals
 };
 
@@ -763,27 +762,32 @@ __device__ __forceinline__ float vec_sum(const float (&w)[N]) {
   return a[0];
 }
 
-// Weights of a lane's chunk: per vector, the fp32 sums of r and p.
+// The weights of a lane's chunk summed: per vector the fp32 sum of r (which
+// is p where there is no q), the vectors added in fp64.
 template <typename In>
-__device__ __forceinline__ void chunk_weights(const ResidCoef& kc, const uint4 (&t)[kU],
-                                              const uint4 (&d)[kU], float (&wr)[kU],
-                                              float (&wp)[kU]) {
+__device__ __forceinline__ double chunk_rsum(const ResidCoef& kc, const uint4 (&t)[kU],
+                                             const uint4 (&d)[kU]) {
   constexpr int VEC = Elem<In>::VEC;
+  double acc = 0.0;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    float r[VEC], p[VEC];
+    float r[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p[e], r[e]);
-    wr[u] = vec_sum<VEC>(r);
-    wp[u] = vec_sum<VEC>(p);
+    for (int e = 0; e < VEC; ++e) {
+      float p;
+      resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p, r[e]);
+    }
+    acc += (double)vec_sum<VEC>(r);
   }
+  return acc;
 }
 
 // ================================================================ k_decide
 
 constexpr int kDecideWaves = 16;
 constexpr int kDecideBlock = kDecideWaves * kLanes;
+
+constexpr int kTotRegs = 4;  // chunk totals the drawing wave keeps in registers (x 64)
 
 struct DecideLds {
   RowStat rs[kMaxK + 1];
@@ -896,9 +900,10 @@ __device__ __forceinline__ void decide_sequence(const Params& P, int b, const De
 // each time the first whose running total passes u*Z among positive
 // weights, or the last positive one if rounding leaves none.
 template <typename In>
-__device__ __forceinline__ int resid_draw(const Params& P, const double* tot, const In* trow,
-                                          const In* drow, const ResidCoef& kc, bool use_r,
-                                          double Z, double u) {
+__device__ __forceinline__ int resid_draw(const Params& P, const double* tot,
+                                          const double (&tc)[kTotRegs], const In* trow,
+                                          const In* drow, const ResidCoef& kc, double Z,
+                                          double u) {
   constexpr int VEC = Elem<In>::VEC;
   constexpr int64_t SLAB = slab_elems<In>();
   const int lane = lane_id();
@@ -910,7 +915,14 @@ __device__ __forceinline__ int resid_draw(const Params& P, const double* tot, co
   double before = 0.0, before_last = 0.0, carry = 0.0;
   for (int g = 0; g < cpr; g += kLanes) {
     const int ch = g + lane;
-    const double w = ch < cpr ? ld_dev(tot + ch) : 0.0;
+    double w = 0.0;
+    if (cpr <= kTotRegs * kLanes) {
+#pragma unroll
+      for (int q = 0; q < kTotRegs; ++q)
+        if (q * kLanes == g) w = tc[q];
+    } else if (ch < cpr) {
+      w = ld_dev(tot + ch);
+    }
     const double incl = carry + wave_inclusive_scan(w);
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = carry;
@@ -952,8 +964,8 @@ __device__ __forceinline__ int resid_draw(const Params& P, const double* tot, co
     for (int e = 0; e < VEC; ++e)
       resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p[e], r[e]);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) w[u][e] = use_r ? r[e] : p[e];
-    vsum[u] = use_r ? vec_sum<VEC>(r) : vec_sum<VEC>(p);
+    for (int e = 0; e < VEC; ++e) w[u][e] = r[e];
+    vsum[u] = vec_sum<VEC>(r);
   }
   int ustar = -1, lstar = 0, ulast = -1, llast = 0;
   double my_ex[kU];  // this lane's running total before its vector, per slab
@@ -1100,7 +1112,6 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const In* trow = trow_ptr<In>(P, b, jr);
   const In* drow = has_q ? drow_ptr<In>(P, b, jr) : nullptr;
   double* ctr = P.ws.ctr + task * (int64_t)P.cpr;
-  double* ctp = P.ws.ctp + task * (int64_t)P.cpr;
   {
     constexpr int VEC = Elem<In>::VEC;
     constexpr int64_t SLAB = slab_elems<In>();
@@ -1124,13 +1135,8 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
       }
     };
     auto sum = [&](const uint4 (&t)[kU], const uint4 (&d)[kU], int ch) {
-      float wr[kU], wp[kU];
-      chunk_weights<In>(kc, t, d, wr, wp);
-      double lr = 0.0, lp = 0.0;
-#pragma unroll
-      for (int u = 0; u < kU; ++u) { lr += (double)wr[u]; lp += (double)wp[u]; }
-      const double cr = wave_sum(lr), cp = wave_sum(lp);
-      if (lane == 0) { st_dev(ctr + ch, cr); st_dev(ctp + ch, cp); }
+      const double cr = wave_sum(chunk_rsum<In>(kc, t, d));
+      if (lane == 0) st_dev(ctr + ch, cr);
     };
     if (c0 < c1) {
       load(ta, da, c0);
@@ -1151,23 +1157,53 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   if (!arrive_last(P.ws.cnt + task * kCtrStride, (unsigned)P.nbs)) return;
 
   // 5. the last block: totals (chunk order) and the draw
-  double zr = 0.0, zp = 0.0;
-  for (int g = 0; g < P.cpr; g += kLanes) {
-    const int ch = g + lane;
-    zr += wave_sum(ch < P.cpr ? ld_dev(ctr + ch) : 0.0);
-    zp += wave_sum(ch < P.cpr ? ld_dev(ctp + ch) : 0.0);
+  double z = 0.0;
+  double tc[kTotRegs];  // chunk totals g * 64 + lane, for rows of up to 64 * kTotRegs chunks
+#pragma unroll
+  for (int g = 0; g < kTotRegs; ++g) {
+    const int ch = g * kLanes + lane;
+    tc[g] = (ch < P.cpr) ? ld_dev(ctr + ch) : 0.0;
+  }
+  if (P.cpr <= kTotRegs * kLanes) {
+#pragma unroll
+    for (int g = 0; g < kTotRegs; ++g) z += wave_sum(tc[g]);
+  } else {
+    for (int g = 0; g < P.cpr; g += kLanes) z += wave_sum(g + lane < P.cpr ? ld_dev(ctr + g + lane) : 0.0);
   }
   if (P.mode == kResidual && P.rows_all && lane == 0) {
     RowRec rr;
     rr.tm = R.tm; rr.targ = R.targ; rr.ts = R.ts;
     rr.dm = R.dm; rr.ds = R.ds; rr.valid = R.valid;
-    rr.zr = zr; rr.zp = zp;
+    rr.zr = z;
     P.ws.rows[(int64_t)b * K1 + jr] = rr;
   }
   if (!draw_row) return;
-  const bool use_r = has_q && zr > 0.0;
-  const int tok = resid_draw<In>(P, use_r ? ctr : ctp, trow, drow, kc, use_r,
-                                 use_r ? zr : zp, (double)P.u_rec[(int64_t)b * K1 + jr]);
+  ResidCoef kd = kc;
+  if (!(z > 0.0)) {
+    // a residual of total zero (p = q throughout): draw from p_n; its chunk
+    // totals are summed here, one chunk at a time
+    kd.has_q = false;
+    z = 0.0;
+    for (int ch = 0; ch < P.cpr; ++ch) {
+      uint4 t[kU], d[kU];
+      const int sl = ch * kU;
+      const int nv = min(kU, P.nslab - sl);
+      load_chunk<In>(trow, sl * (int)slab_elems<In>() + lane * Elem<In>::VEC, nv, P.V, false, t);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) d[u] = make_uint4(0, 0, 0, 0);
+      const double cr = wave_sum(chunk_rsum<In>(kd, t, d));
+      if (lane == 0) st_dev(ctr + ch, cr);
+      z += cr;
+      if (ch < kTotRegs * kLanes) {
+#pragma unroll
+        for (int g = 0; g < kTotRegs; ++g)
+          if (g * kLanes + lane == ch) tc[g] = cr;
+      }
+    }
+    vm_complete();
+  }
+  const int tok = resid_draw<In>(P, ctr, tc, trow, drow, kd, z,
+                                 (double)P.u_rec[(int64_t)b * K1 + jr]);
   if (lane == 0) P.out_token[b] = tok;
 }
 
@@ -1288,7 +1324,7 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) 
 // ================================================================ host side
 
 struct Layout {
-  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, cn, cpos, ctr, ctp, cnt, total;
+  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, cn, cpos, ctr, cnt, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1322,7 +1358,6 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   L.cn = take(F > 0 ? sizeof(int) * RS : 0);
   L.cpos = take(F > 0 ? sizeof(int) * RS * kDumpCap : 0);
   L.ctr = take(sizeof(double) * R * cpr);
-  L.ctp = take(sizeof(double) * R * cpr);
   L.cnt = take(sizeof(unsigned) * R * kCtrStride);
   L.total = o;
   return L;
@@ -1346,7 +1381,6 @@ static Ws bind_ws(void* base, const Layout& L) {
   w.cpos = reinterpret_cast<int*>(p + L.cpos);
   w.yd = reinterpret_cast<float*>(p + L.yd);
   w.ctr = reinterpret_cast<double*>(p + L.ctr);
-  w.ctp = reinterpret_cast<double*>(p + L.ctp);
   w.cnt = reinterpret_cast<unsigned*>(p + L.cnt);
   return w;
 }
