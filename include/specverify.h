@@ -35,8 +35,8 @@
  *    m.111cn.net translation, section 基准测试).
  *
  * Shapes and layout.  B sequences, k drafted positions (1 <= k <= 63),
- * positions j = 0..k where j = k is the bonus position, vocabulary V >= 2
- * shared by target and drafter (speculative-sampling page, "Quick Start &
+ * positions j = 0..k where j = k is the bonus position, vocabulary
+ * 2 <= V <= 1048576 shared by target and drafter (speculative-sampling page, "Quick Start &
  * Requirements": both models must share one vocabulary).  Logits are
  * [B][k+1][V] with V contiguous, addressed with element strides; every row
  * start must be 16-byte aligned (so strides must be multiples of 4 fp32 /
@@ -160,10 +160,11 @@ sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows,
  *   p_draft, q_draft [B][k] out (nullable): p_j(d_j), q_j(d_j) (one-hot
  *                      indicators at temperature 0).  Passing q_draft makes
  *                      the draft rows be read also at temperature 0.
- * Launches: statistics kernel (one wave per 4096-element chunk of a row,
- * rows merged and sequences decided by the last wave to finish), then a
- * residual kernel that re-reads only row n of the temperature > 0
- * sequences. */
+ * Launches: a streaming statistics kernel (one resident round of waves,
+ * each over an equal slab range of one row, writing per-range partials),
+ * then a decision kernel that merges the partials per row, decides each
+ * sequence, ranks the forks, and re-reads only row n of the temperature > 0
+ * sequences for the draw. */
 sv_status sv_verify(const sv_batch* in, const float* u_accept,
                     const float* u_recover, int32_t* accept_len,
                     int32_t* out_token, float* p_draft, float* q_draft,
