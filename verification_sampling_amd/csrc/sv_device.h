@@ -139,14 +139,30 @@ __device__ __forceinline__ void set_neg_inf(uint4& v, int e) {
 template <typename In>
 __device__ __forceinline__ void load_vec(const In* __restrict__ row, int e0, int V, uint4& v);
 
+#ifndef SV_NT_LOADS
+#define SV_NT_LOADS 1
+#endif
+
+// One 16-byte load of streamed logits.  Every byte of a row is read once per
+// pass, so the loads are marked non-temporal: the lines are not kept in the
+// caches for reuse.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+#if SV_NT_LOADS
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
 template <typename In>
 __device__ __forceinline__ void load_chunk(const In* __restrict__ row, int e_base, int nvalid,
                                            int V, bool full, uint4 (&raw)[kU]) {
   constexpr int SLAB = slab_elems<In>();
   if (full) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-      raw[u] = *reinterpret_cast<const uint4*>(row + e_base + u * SLAB);
+    for (int u = 0; u < kU; ++u) raw[u] = load_stream16(row + e_base + u * SLAB);
   } else {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
