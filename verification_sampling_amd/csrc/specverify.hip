@@ -490,20 +490,22 @@ __device__ __forceinline__ Merged merge_lanes(float mi, double si, int ai, bool 
 // a round of 64 * kRound at a time; their elements (id < V, id != mask_id)
 // at or above the F-th largest of the lanes' maxima over the loaded
 // vectors go into this lane's list.  That bound never drops one of the
-// row's top-F: at least F of the loaded elements reach it.
+// row's top-F: at least F of the loaded elements reach it.  With nhalf = 2,
+// two waves share the row: wave `half` takes every other round.
 template <typename In, int F>
 __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, int64_t base,
-                                                int np, int cnt, int mask_id, TopList<F>& mine) {
+                                                int np, int cnt, int mask_id, int half,
+                                                int nhalf, TopList<F>& mine) {
   if constexpr (F > 0) {
     constexpr int VEC = Elem<In>::VEC;
-    constexpr int kRound = 4;
+    constexpr int kRound = 2;
     const int lane = lane_id();
     const int mycnt = lane < np ? cnt : 0;
     const int incl = wave_inclusive_scan_i(mycnt);
     const int total = readlane_i(incl, kLanes - 1);
     const In* drow = drow_ptr<In>(P, b, j);
     const int V = P.V;
-    for (int t0 = 0; t0 < total; t0 += kLanes * kRound) {
+    for (int t0 = half * kLanes * kRound; t0 < total; t0 += nhalf * kLanes * kRound) {
       int pos[kRound];
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
@@ -569,22 +571,27 @@ struct RowStat {
 // The row's forks: the top-f of the segments' lists and of the candidate
 // vectors they passed on, with masked-softmax probabilities at tau
 // (2^((v - m') c) / S', (1, 0, ...) at temperature 0); lane r < f gets entry
-// r in (tok, prob).
+// r in (tok, prob).  With nhalf = 2 this wave ranks its half of the
+// candidates (the segments' lists go to half 0) and top is that half's
+// top-f, to be merged with the other half's.
 template <typename In, int F>
 __device__ __forceinline__ void fork_top(const Params& P, int b, int j, const RowPlan& pl,
                                          const float (&lv)[F > 0 ? F : 1],
                                          const int (&li)[F > 0 ? F : 1], int cnt, float qm,
-                                         double qs, double cd, TopList<F>& top, int& tok,
-                                         float& prob) {
+                                         double qs, double cd, int half, int nhalf,
+                                         TopList<F>& top, int& tok, float& prob) {
   const int lane = lane_id();
   tok = kEmptyId;
   prob = 0.0f;
   if constexpr (F > 0) {
     TopList<F> mine;
     mine.clear();
+    if (half == 0) {
 #pragma unroll
-    for (int r = 0; r < F; ++r) mine.insert(lv[r], li[r]);
-    fork_candidates<In, F>(P, b, j, slot_of(P, b, j) * kMaxSeg, P.nparts, cnt, pl.mask_id, mine);
+      for (int r = 0; r < F; ++r) mine.insert(lv[r], li[r]);
+    }
+    fork_candidates<In, F>(P, b, j, slot_of(P, b, j) * kMaxSeg, P.nparts, cnt, pl.mask_id, half,
+                           nhalf, mine);
     wave_merge_lists<F>(mine, P.f, top);
     float v = neg_inf();
 #pragma unroll
@@ -600,10 +607,13 @@ __device__ __forceinline__ void fork_top(const Params& P, int b, int j, const Ro
 // Merges the partials of row (b, j) into rs (written by lanes 0..f-1 and
 // lane 0).  One wave; every load is issued before the first is used (the
 // partials, the fork lists and the drafted token's logits as seen by
-// k_stats are loaded whether or not the row needs them).
+// k_stats are loaded whether or not the row needs them).  With nhalf = 2
+// two waves share the row's forks: both merge the statistics, half 0
+// writes rs, and each writes its half's top-f list to (hv, hi).
 template <typename In, int F>
 __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float tau, RowStat* rs,
-                                         bool forks_now) {
+                                         bool forks_now, int half = 0, int nhalf = 1,
+                                         float* hv = nullptr, int* hi = nullptr) {
   const int lane = lane_id();
   const Ws& W = P.ws;
   const int k = P.k;
@@ -655,14 +665,22 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
   top.clear();
   if (pl.readD) {
     const Merged q = merge_lanes(dmi, dsi, dai, pl.greedy, cd);
-    if (lane == 0) { rs->qm = q.m; rs->qs = q.s; }
+    if (lane == 0 && half == 0) { rs->qm = q.m; rs->qs = q.s; }
     if (pl.topf) {
       if constexpr (F > 0) {
         if (forks_now) {
           int tok;
           float prob;
-          fork_top<In, F>(P, b, j, pl, lv, li, cnt, q.m, q.s, cd, top, tok, prob);
-          if (lane < P.f) { rs->ftok[lane] = tok; rs->fprob[lane] = prob; }
+          fork_top<In, F>(P, b, j, pl, lv, li, cnt, q.m, q.s, cd, half, nhalf, top, tok, prob);
+          if (nhalf > 1) {
+#pragma unroll
+            for (int r = 0; r < F; ++r) {
+              if (lane == r && r < P.f) { hv[r] = top.v[r]; hi[r] = top.i[r]; }
+            }
+          } else if (lane < P.f) {
+            rs->ftok[lane] = tok;
+            rs->fprob[lane] = prob;
+          }
         }
       }
       if (j < k) {
@@ -701,7 +719,7 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
       }
     }
   }
-  if (lane == 0) {
+  if (lane == 0 && half == 0) {
     rs->tm = tm; rs->targ = targ; rs->ts = ts;
     rs->dm = dm; rs->darg = darg; rs->ds = ds;
     rs->pd = pd; rs->qd = qd;
@@ -791,6 +809,8 @@ constexpr int kTotRegs = 4;  // chunk totals the drawing wave keeps in registers
 
 struct DecideLds {
   RowStat rs[kMaxK + 1];
+  float hv[kMaxK + 1][2][kMaxF];  // fork blocks: each half's top-f per row
+  int hi[kMaxK + 1][2][kMaxF];
   int n, status;
 };
 
@@ -1033,7 +1053,13 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
     const int b = (int)(blockIdx.x - ntasks * P.nbs);
     const float tau = P.tau[b];
     if (!(tau > 0.0f && tau_ok(tau))) return;  // the owner block ranks these
-    for (int j = w; j < K1; j += kDecideWaves) row_stat<In, F>(P, b, j, tau, &S.rs[j], true);
+    // two waves per row when the block has them: wave t ranks half t / K1
+    // of row t % K1's candidates
+    const int nhalf = (2 * K1 <= kDecideWaves) ? 2 : 1;
+    for (int t = w; t < K1 * nhalf; t += kDecideWaves) {
+      const int j = t % K1, h = t / K1;
+      row_stat<In, F>(P, b, j, tau, &S.rs[j], true, h, nhalf, S.hv[j][h], S.hi[j][h]);
+    }
     __syncthreads();
     if (w == 0) {
       int n, status;
@@ -1043,6 +1069,34 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
     __syncthreads();
     if (S.status == 0) return;
     for (int j = w; j < K1; j += kDecideWaves) {
+      if constexpr (F > 0) {
+        if (nhalf > 1) {
+          // the two halves' lists merged (lane h * f + r holds entry r of half h)
+          TopList<F> l, top;
+          l.clear();
+          if (lane < 2 * P.f) {
+            const int h = lane / P.f, r = lane - h * P.f;
+            l.insert(S.hv[j][h][r], S.hi[j][h][r]);
+          }
+          wave_merge_lists<F>(l, P.f, top);
+          const float qm = S.rs[j].qm;
+          const double qs = S.rs[j].qs;
+          const double cd = (double)scale_of(tau);
+#pragma unroll
+          for (int r = 0; r < F; ++r) {
+            if (lane == r && r < P.f) {
+              const float v = top.v[r];
+              const float prob = (!finitef(qm) || !(v > neg_inf()))
+                                     ? 0.0f
+                                     : (float)(exp2(((double)v - (double)qm) * cd) / qs);
+              const int64_t o = ((int64_t)b * K1 + j) * P.f + r;
+              P.fork_tok[o] = top.i[r];
+              if (P.fork_prob) P.fork_prob[o] = prob;
+            }
+          }
+          continue;
+        }
+      }
       if (lane < P.f) {
         const int64_t o = ((int64_t)b * K1 + j) * P.f + lane;
         P.fork_tok[o] = S.rs[j].ftok[lane];
