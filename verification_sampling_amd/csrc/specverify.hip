@@ -841,24 +841,50 @@ __device__ __forceinline__ void write_seq_error(const Params& P, int b) {
 // (ballot over positions) and, when write_outputs, the per-sequence outputs.
 // Returns the outcome position n and the status (0 error, 1 finished,
 // 2 draw pending).
+// The per-sequence inputs of the decision, loaded by wave 0 at the start of
+// the kernel so that they arrive together with the row partials: lane j < k
+// holds the drafted token and the acceptance uniform of position j.
+struct SeqIn {
+  float tau;
+  int d;
+  float ua;
+  int pos;
+};
+
+__device__ __forceinline__ SeqIn load_seq_inputs(const Params& P, int b) {
+  const int lane = lane_id();
+  SeqIn in;
+  in.tau = P.tau[b];
+  in.d = 0;
+  in.ua = 0.0f;
+  in.pos = -1;
+  if (lane < P.k) {
+    in.d = P.drafts[(int64_t)b * P.k + lane];
+    if (P.mode == kVerify) in.ua = P.u_acc[(int64_t)b * P.k + lane];
+  }
+  if (P.mode == kResidual) in.pos = P.position[b];
+  return in;
+}
+
 __device__ __forceinline__ void decide_sequence(const Params& P, int b, const DecideLds& S,
-                                                bool write_outputs, int& n_out, int& status) {
+                                                const SeqIn& in, bool write_outputs, int& n_out,
+                                                int& status) {
   const int lane = lane_id();
   const int k = P.k;
   const int K1 = k + 1;
-  const float tau = P.tau[b];
+  const float tau = in.tau;
   const bool tok = tau_ok(tau);
   const bool greedy = tau == 0.0f;
 
   bool ok = tok;
   int d = 0;
   if (lane < k) {
-    d = P.drafts[(int64_t)b * k + lane];
+    d = in.d;
     if (d < 0 || d >= P.V) ok = false;
   }
   int pos = -1;
   if (P.mode == kResidual) {
-    pos = P.position[b];
+    pos = in.pos;
     if (pos < 0 || pos > k) ok = false;
   }
   // rows read are valid
@@ -885,7 +911,7 @@ __device__ __forceinline__ void decide_sequence(const Params& P, int b, const De
         // a = min(1, p/q); q = 0: a = 1 if p > 0 else 0.  Accept iff u < a.
         const double p = r.pd, q = r.qd;
         const double a = (q == 0.0) ? (p > 0.0 ? 1.0 : 0.0) : fmin(1.0, p / q);
-        acc = (double)P.u_acc[(int64_t)b * k + lane] < a;
+        acc = (double)in.ua < a;
       }
       if (write_outputs) {
         if (P.p_draft) P.p_draft[(int64_t)b * k + lane] = (float)r.pd;
@@ -1056,6 +1082,8 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
     // two waves per row when the block has them: wave t ranks half t / K1
     // of row t % K1's candidates
     const int nhalf = (2 * K1 <= kDecideWaves) ? 2 : 1;
+    SeqIn sin;
+    if (w == 0) sin = load_seq_inputs(P, b);
     for (int t = w; t < K1 * nhalf; t += kDecideWaves) {
       const int j = t % K1, h = t / K1;
       row_stat<In, F>(P, b, j, tau, &S.rs[j], true, h, nhalf, S.hv[j][h], S.hi[j][h]);
@@ -1063,7 +1091,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
     __syncthreads();
     if (w == 0) {
       int n, status;
-      decide_sequence(P, b, S, false, n, status);
+      decide_sequence(P, b, S, sin, false, n, status);
       if (lane == 0) S.status = status;
     }
     __syncthreads();
@@ -1122,6 +1150,8 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   // owner at temperature 0 (the greedy q(d) needs the draft's top-1) and for
   // the forks-only call; at temperature > 0 a fork block of their own does.
   const bool forks_now = owner && (P.mode == kForks || !(tau > 0.0f && tau_ok(tau)));
+  SeqIn sin;
+  if (w == 0) sin = load_seq_inputs(P, b);
   if (P.mode == kResidual && !P.rows_all) {
     if (w == 0) {
       const int pos = P.position[b];
@@ -1135,7 +1165,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   // 2. decision
   if (w == 0) {
     int n, status;
-    decide_sequence(P, b, S, owner, n, status);
+    decide_sequence(P, b, S, sin, owner, n, status);
     if (lane == 0) { S.n = n; S.status = status; }
     if (owner && lane == 0) { P.ws.seqs[b].n = n; P.ws.seqs[b].status = status; }
   }
