@@ -8,6 +8,7 @@ does, and shares no code with it.
 from .specverify_oracle import (BF16, F32, FLAG_BAND, BatchResult, ProbVerdict,
                                 RowError, SequenceResult,
                                 acceptance_probability, argmax_first,
+                                cache_hit, cache_hits_batch,
                                 first_rejection, forked_topf,
                                 forked_topf_batch, inverse_cdf,
                                 residual_distribution, residual_weights,
@@ -17,7 +18,8 @@ from .specverify_oracle import (BF16, F32, FLAG_BAND, BatchResult, ProbVerdict,
 
 __all__ = ["BF16", "F32", "FLAG_BAND", "BatchResult", "ProbVerdict",
            "RowError", "SequenceResult", "acceptance_probability",
-           "argmax_first", "first_rejection", "forked_topf",
+           "argmax_first", "cache_hit", "cache_hits_batch",
+           "first_rejection", "forked_topf",
            "forked_topf_batch", "inverse_cdf", "residual_distribution",
            "residual_weights", "sample_at_position", "softmax_rows",
            "softmax_temp", "verify_batch", "verify_from_probs",

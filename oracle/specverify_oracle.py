@@ -498,3 +498,35 @@ def forked_topf_batch(draft, dtype, draft_tokens, temperature, f):
             toks[b, j], probs[b, j] = forked_topf(rows[j], tau, f,
                                                   ds[j] if j < k else None)
     return toks, probs
+
+def cache_hit(fork_tokens_n, token) -> int:
+    """Speculation-cache lookup of one verification outcome.
+
+    [SSD-editorial] "What changes in SSD": the drafter speculates ahead of
+    time for the likely verification outcomes, and when one of its guesses
+    is right the speculation is returned at once.  [SSD-summary], the
+    async-SD utilities file: the forked recovery tokens (top-k with the
+    drafted token masked) are what handles the cache hits and misses.  The
+    outcome of a step is (n, token); the drafter speculated, at position n,
+    for the f forked tokens ``fork_tokens_n``.  The outcome hits when
+    ``token`` is one of them: the result is its index r (the forks are
+    distinct, so there is at most one), else -1.
+    """
+    for r, t in enumerate(fork_tokens_n):
+        if int(t) == int(token):
+            return r
+    return -1
+
+
+def cache_hits_batch(fork_tokens, accept_len, token) -> np.ndarray:
+    """cache_hit for every sequence of a batch: fork_tokens [B, k+1, f],
+    accept_len [B] (the outcome position n), token [B].  A sequence whose
+    outcome is an error (n or token negative) gets -1."""
+    fork_tokens = np.asarray(fork_tokens)
+    B, K1, _ = fork_tokens.shape
+    out = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        n, t = int(accept_len[b]), int(token[b])
+        if 0 <= n < K1 and t >= 0:
+            out[b] = cache_hit(fork_tokens[b, n], t)
+    return out

@@ -303,3 +303,62 @@ def test_sample_at_position_agrees_with_verify():
             w.target[i], w.draft[i], "bf16", w.draft_tokens[i],
             w.temperature[i], r.accept_len[i], w.u_recover[i])
         assert not err and tok == r.token[i]
+
+
+# ---------------------------------------------------------------- cache hits
+
+def test_cache_hit_matches_numpy_search():
+    """The hit index is the position of the outcome token in the forks of the
+    outcome position (numpy's search over the same table), -1 on a miss or
+    an error outcome."""
+    rng = np.random.default_rng(5)
+    B, K1, f, V = 40, 6, 3, 20
+    forks = np.stack([np.stack([rng.choice(V, f, replace=False) for _ in range(K1)])
+                      for _ in range(B)])
+    n = rng.integers(-1, K1, B)
+    tok = rng.integers(-1, V, B)
+    got = oracle.cache_hits_batch(forks, n, tok)
+    for b in range(B):
+        if n[b] < 0 or tok[b] < 0:
+            assert got[b] == -1
+            continue
+        idx = np.flatnonzero(forks[b, n[b]] == tok[b])
+        assert got[b] == (idx[0] if idx.size else -1)
+    assert (got >= 0).any() and (got == -1).any()
+
+
+def test_hand_worked_cache_hit_and_miss():
+    """k = 1, V = 6.  The target puts almost all mass on token 4 and the
+    drafter most of its mass on token 1 (logit 5 against at most 3), so
+    drafted token 1 is rejected at position 0 (p/q < e^-19) and the residual
+    max(0, p - q), which is positive only at token 4, draws token 4 for any
+    u.  Forks at position 0 (token 1 masked, f = 2): draft row
+    (-1, 5, 3, 2, 2.5, -3) gives 2 then 4, so the outcome (0, 4) hits at
+    index 1; with the row (-1, 5, 3, 2, 0, -3) the forks are 2 then 3 and
+    the same outcome misses."""
+    T = np.array([[-10, -10, -10, -10, 10, -10], [0, 0, 0, 0, 0, 0]], dtype=np.float64)
+    for drow, want_forks, want_hit in (([-1, 5, 3, 2, 2.5, -3], [2, 4], 1),
+                                       ([-1, 5, 3, 2, 0, -3], [2, 3], -1)):
+        D = np.array([drow, [0, 0, 0, 0, 0, 0]], dtype=np.float64)
+        r = oracle.verify_sequence(T, D, "f32", [1], 1.0, [0.5], [0.5, 0.5], f=2)
+        assert (r.accept_len, r.token) == (0, 4)
+        assert list(r.fork_tokens[0]) == want_forks
+        assert oracle.cache_hit(r.fork_tokens[0], r.token) == want_hit
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.8])
+def test_cache_hit_invariants_on_synthetic_batches(tau):
+    """A hit names the outcome token among the forks of the outcome
+    position; it never names the rejected draft, which the forks exclude."""
+    w = _small_zipf(12, 5, 3000, tau, 23)
+    r = oracle.verify_batch(w.target, w.draft, "bf16", w.draft_tokens,
+                            w.temperature, w.u_accept, w.u_recover, f=3)
+    hits = oracle.cache_hits_batch(r.fork_tokens, r.accept_len, r.token)
+    for i in range(w.B):
+        n = r.accept_len[i]
+        if hits[i] >= 0:
+            assert r.fork_tokens[i, n, hits[i]] == r.token[i]
+        else:
+            assert r.token[i] not in list(r.fork_tokens[i, n])
+        if n < w.k:
+            assert w.draft_tokens[i, n] not in list(r.fork_tokens[i, n])
