@@ -107,11 +107,15 @@ typedef struct sv_batch {
  * [B][k+1][f] fp32 (nullable), 1 <= f <= min(16, V-1).  Probabilities are
  * the softmax at the sequence temperature of the draft logits with the
  * drafted token masked out (nothing masked at j = k); (1, 0, ...) at
- * temperature 0. */
+ * temperature 0.
+ * hits [B] int32 (nullable; sv_verify only, ignored by sv_forked_topf):
+ * the speculation-cache lookup of each sequence's outcome, as computed by
+ * sv_cache_hit from this call's forks, accept_len and out_token. */
 typedef struct sv_forks {
   int32_t f;
   int32_t* tokens;
   float* probs;
+  int32_t* hits;
 } sv_forks;
 
 /* Optional per-call extras.  ev_stats_begin / ev_stats_end: hipEvent_t
@@ -164,7 +168,8 @@ sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows,
  * each over an equal slab range of one row, writing per-range partials),
  * then a decision kernel that merges the partials per row, decides each
  * sequence, ranks the forks, and re-reads only row n of the temperature > 0
- * sequences for the draw. */
+ * sequences for the draw; with forks->hits, then the lookup of
+ * sv_cache_hit. */
 sv_status sv_verify(const sv_batch* in, const float* u_accept,
                     const float* u_recover, int32_t* accept_len,
                     int32_t* out_token, float* p_draft, float* q_draft,
@@ -200,6 +205,25 @@ sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,
  * logits).  in->target may be NULL. */
 sv_status sv_forked_topf(const sv_batch* in, const sv_forks* forks, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* Speculation-cache lookup of verification outcomes.  In SSD the drafter
+ * speculates ahead of time for the likely outcomes of verification and a
+ * correct guess is returned at once ("What changes in SSD", hysenlabs.com
+ * editorial); the forked recovery tokens are the guesses, and they decide
+ * cache hits and misses (tanishqkumar/ssd repository summary, async-SD
+ * utilities file).  The outcome of sequence b is (n, t) = (accept_len[b],
+ * out_token[b]); the drafter speculated, at position n, for the f tokens
+ * fork_tokens[b][n][0..f-1].
+ *   fork_tokens [B][k+1][f] int32, accept_len [B], out_token [B] (device,
+ *                 caller-owned; e.g. the outputs of sv_verify, or forks
+ *                 from an earlier sv_forked_topf on the drafter's side)
+ *   hits [B] int32 out: the index r with fork_tokens[b][n][r] == t (the
+ *                 first, if tokens repeat), else -1; -1 also when n is
+ *                 outside [0, k] or t < 0 (an error outcome).
+ * 1 <= k <= 63, 1 <= f <= 16, B >= 0.  One small kernel; no workspace. */
+sv_status sv_cache_hit(int32_t B, int32_t k, int32_t f,
+                       const int32_t* fork_tokens, const int32_t* accept_len,
+                       const int32_t* out_token, int32_t* hits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -77,6 +77,14 @@ def compare_verify(out, ref, seqs, f, k, want_p=True, want_q=True):
         ft = out["fork_tokens"].cpu().numpy()[seqs]
         np.testing.assert_array_equal(ft, ref.fork_tokens, err_msg="fork tokens")
         assert_probs_close(out["fork_probs"].cpu().numpy()[seqs], ref.fork_probs, "fork probs")
+    if f and "cache_hit" in out:
+        # the oracle's lookup of its own outcome in its own forks
+        ref_hits = oracle.cache_hits_batch(ref.fork_tokens, ref.accept_len, ref.token)
+        hits = out["cache_hit"].cpu().numpy()[seqs]
+        for i in range(len(seqs)):
+            if ref.flagged[i] and not ref.error[i]:
+                continue
+            assert hits[i] == ref_hits[i], (int(seqs[i]), int(hits[i]), int(ref_hits[i]))
     return n_flag, len(seqs)
 
 

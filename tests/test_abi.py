@@ -129,3 +129,17 @@ def test_softmax_validation(L):
     assert call(ostride=1001) == MISALIGNED
     assert call(wsb=64) == WORKSPACE
     assert call(logits=None) == INVALID
+
+
+def test_cache_hit_validation(L):
+    p = ctypes.c_void_p(FAKE)
+    assert L.sv_cache_hit(0, 7, 3, None, None, None, None, None) == OK   # empty batch
+    assert L.sv_cache_hit(-1, 7, 3, p, p, p, p, None) == INVALID
+    assert L.sv_cache_hit(4, 0, 3, p, p, p, p, None) == INVALID
+    assert L.sv_cache_hit(4, 64, 3, p, p, p, p, None) == INVALID
+    assert L.sv_cache_hit(4, 7, 0, p, p, p, p, None) == INVALID
+    assert L.sv_cache_hit(4, 7, 17, p, p, p, p, None) == INVALID
+    for i in range(4):
+        args = [p, p, p, p]
+        args[i] = None
+        assert L.sv_cache_hit(4, 7, 3, *args, None) == INVALID

@@ -43,7 +43,7 @@ def run_case(sv, T, D, dtype, drafts, tau, ua, ur, f, want_q=True):
     x = dict(T=padded_dev(T, dtype), D=padded_dev(D, dtype))
     out = sv.verify(x["T"], x["D"], torch.from_numpy(drafts).cuda(), torch.from_numpy(tau).cuda(),
                     torch.from_numpy(ua).cuda(), torch.from_numpy(ur).cuda(), f=f,
-                    want_p=True, want_q=want_q)
+                    want_p=True, want_q=want_q, want_hits=f > 0)
     torch.cuda.synchronize()
     ref = oracle.verify_batch(T, D, dtype, drafts, tau, ua, ur, f=f, want_q=want_q)
     nf, n = compare_verify(out, ref, np.arange(T.shape[0]), f, drafts.shape[1], want_q=want_q)
@@ -135,6 +135,7 @@ def test_error_sequences(sv):
     assert np.all(ft[:6] == -1)
     assert np.all(np.isnan(out["fork_probs"].cpu().numpy()[:6]))
     assert np.all(np.isnan(out["p_draft"].cpu().numpy()[:6]))
+    assert np.all(out["cache_hit"].cpu().numpy()[:6] == -1)
     log("[edges] error sequences: ok")
 
 

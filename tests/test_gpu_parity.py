@@ -36,7 +36,7 @@ def sv():
 
 def run_verify(sv, w, x, f):
     out = sv.verify(x["T"], x["D"], x["d"], x["tau"], x["ua"], x["ur"], f=f,
-                    want_p=True, want_q=True)
+                    want_p=True, want_q=True, want_hits=f > 0)
     torch.cuda.synchronize()
     return out
 
@@ -98,6 +98,17 @@ def _properties(out, w, f):
                 if j < k:
                     assert w.draft_tokens[b, j] not in ft[b, j]
         assert np.all(np.diff(fp, axis=-1) <= 0)
+        # cache hits: the outcome token among the forks of the outcome
+        # position; the standalone lookup agrees with the fused one
+        hits = out["cache_hit"].cpu().numpy()
+        for b in range(w.B):
+            row = list(ft[b, al[b]])
+            assert hits[b] == (row.index(tok[b]) if tok[b] in row else -1), b
+        from verification_sampling_amd import specverify
+        alone = specverify.cache_hit(out["fork_tokens"], out["accept_len"], out["out_token"])
+        torch.cuda.synchronize()
+        assert torch.equal(alone, out["cache_hit"])
+        log(f"[parity] cache hits {int((hits >= 0).sum())}/{w.B}")
 
 
 def test_batched_verify_fork_qwen(sv):

@@ -1394,6 +1394,37 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
   }
 }
 
+// ================================================================ hits
+
+// Speculation-cache lookup, one thread per sequence: the index of the
+// outcome token among the forks of the outcome position, else -1.
+__global__ __launch_bounds__(kBlock) void k_hits(int32_t B, int32_t k, int32_t f,
+                                                 const int32_t* __restrict__ forks,
+                                                 const int32_t* __restrict__ accept_len,
+                                                 const int32_t* __restrict__ out_token,
+                                                 int32_t* __restrict__ hits) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int n = accept_len[b];
+  const int t = out_token[b];
+  int hit = -1;
+  if (n >= 0 && n <= k && t >= 0) {
+    const int32_t* row = forks + (b * (k + 1) + n) * f;
+    for (int r = f - 1; r >= 0; --r)
+      if (row[r] == t) hit = r;
+  }
+  hits[b] = hit;
+}
+
+static hipError_t launch_hits(int32_t B, int32_t k, int32_t f, const int32_t* forks,
+                              const int32_t* accept_len, const int32_t* out_token, int32_t* hits,
+                              hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_hits, dim3((unsigned)((B + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, B,
+                     k, f, forks, accept_len, out_token, hits);
+  return hipGetLastError();
+}
+
 // ================================================================ fill
 
 __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) {
@@ -1673,7 +1704,7 @@ const char* sv_status_string(int32_t s) {
   }
 }
 
-const char* sv_version(void) { return "libspecverify 0.2.0 gfx950"; }
+const char* sv_version(void) { return "libspecverify 0.3.0 gfx950"; }
 
 sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows, int32_t V,
                           int64_t row_stride, const float* temperature, int64_t rows_per_temp,
@@ -1741,6 +1772,11 @@ sv_status sv_verify_ex(const sv_batch* in, const float* u_accept, const float* u
     if (hipEventRecord((hipEvent_t)opts->ev_stats_end, s) != hipSuccess) return SV_ERR_HIP;
   }
   if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
+  if (forks && forks->hits) {
+    if (launch_hits(in->B, in->k, f, forks->tokens, accept_len, out_token, forks->hits, s) !=
+        hipSuccess)
+      return SV_ERR_HIP;
+  }
   return SV_OK;
 }
 
@@ -1801,6 +1837,18 @@ sv_status sv_forked_topf(const sv_batch* in, const sv_forks* forks, void* ws, si
   if (dispatch_stats(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
+}
+
+sv_status sv_cache_hit(int32_t B, int32_t k, int32_t f, const int32_t* fork_tokens,
+                       const int32_t* accept_len, const int32_t* out_token, int32_t* hits,
+                       void* stream) {
+  if (B < 0 || k < 1 || k > kMaxK || f < 1 || f > kMaxF) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!fork_tokens || !accept_len || !out_token || !hits) return SV_ERR_INVALID_ARG;
+  return launch_hits(B, k, f, fork_tokens, accept_len, out_token, hits, (hipStream_t)stream) ==
+                 hipSuccess
+             ? SV_OK
+             : SV_ERR_HIP;
 }
 
 }  // extern "C"

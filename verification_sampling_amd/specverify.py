@@ -41,7 +41,7 @@ class SvBatch(ctypes.Structure):
 
 class SvForks(ctypes.Structure):
     _fields_ = [("f", ctypes.c_int32), ("tokens", ctypes.c_void_p),
-                ("probs", ctypes.c_void_p)]
+                ("probs", ctypes.c_void_p), ("hits", ctypes.c_void_p)]
 
 
 class SvOpts(ctypes.Structure):
@@ -85,6 +85,8 @@ def lib():
             L.sv_residual_sample.restype = i32
             L.sv_forked_topf.argtypes = [pb, pf, vp, sz, vp]
             L.sv_forked_topf.restype = i32
+            L.sv_cache_hit.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+            L.sv_cache_hit.restype = i32
             _lib = L
     return _lib
 
@@ -199,11 +201,12 @@ def _f32(t, shape, name):
 # ------------------------------------------------------------------ API
 
 def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int = 0,
-           want_p: bool = False, want_q: bool = False, workspace: Optional[Workspace] = None,
-           stream=None, out=None, timing_events=None):
+           want_p: bool = False, want_q: bool = False, want_hits: bool = False,
+           workspace: Optional[Workspace] = None, stream=None, out=None, timing_events=None):
     """sv_verify: returns dict with accept_len [B] int32, out_token [B]
-    int32, and optionally p_draft/q_draft [B,k] float32 and fork_tokens
-    [B,k+1,f] int32 / fork_probs [B,k+1,f] float32."""
+    int32, and optionally p_draft/q_draft [B,k] float32, fork_tokens
+    [B,k+1,f] int32 / fork_probs [B,k+1,f] float32 and (f > 0, want_hits)
+    cache_hit [B] int32."""
     b = _batch(target, draft, draft_tokens, temperature)
     B, k = b.B, b.k
     dev = target.device
@@ -221,9 +224,13 @@ def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int
         if f > 0:
             out["fork_tokens"] = torch.empty(B, k + 1, f, dtype=torch.int32, device=dev)
             out["fork_probs"] = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
+            if want_hits:
+                out["cache_hit"] = torch.empty(B, dtype=torch.int32, device=dev)
     forks = None
     if f > 0:
-        forks = SvForks(int(f), out["fork_tokens"].data_ptr(), out["fork_probs"].data_ptr())
+        hits = out.get("cache_hit")
+        forks = SvForks(int(f), out["fork_tokens"].data_ptr(), out["fork_probs"].data_ptr(),
+                        hits.data_ptr() if hits is not None else None)
     ws = workspace or default_workspace(dev, stream)
     buf = ws.get(workspace_size(B, k, b.V, f), ("verify", B, k, b.V, f), stream)
     opts = None
@@ -286,6 +293,26 @@ def forked_topf(draft, draft_tokens, temperature, f: int,
     return toks, probs
 
 
+def cache_hit(fork_tokens, accept_len, out_token, stream=None):
+    """sv_cache_hit: the index of each outcome token among the forks of its
+    outcome position ([B] int32, -1 on a miss).  fork_tokens [B,k+1,f],
+    accept_len [B] and out_token [B]: contiguous int32 on the device."""
+    for t, name in ((fork_tokens, "fork_tokens"), (accept_len, "accept_len"),
+                    (out_token, "out_token")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous int32")
+    if fork_tokens.dim() != 3:
+        raise ValueError("fork_tokens must be [B, k+1, f]")
+    B, K1, f = fork_tokens.shape
+    if tuple(accept_len.shape) != (B,) or tuple(out_token.shape) != (B,):
+        raise ValueError("accept_len and out_token must be [B]")
+    hits = torch.empty(B, dtype=torch.int32, device=fork_tokens.device)
+    code = lib().sv_cache_hit(int(B), int(K1 - 1), int(f), _ptr(fork_tokens), _ptr(accept_len),
+                              _ptr(out_token), _ptr(hits), _stream_handle(stream))
+    _check(code, "sv_cache_hit")
+    return hits
+
+
 def softmax_temp(logits, temperature, rows_per_temp: int = 1,
                  workspace: Optional[Workspace] = None, stream=None):
     """sv_softmax_temp over the rows of a [rows, V] tensor (V contiguous);
@@ -320,8 +347,10 @@ class PreparedVerify:
         B, k = self.batch.B, self.batch.k
         _f32(u_accept, (B, k), "u_accept")
         _f32(u_recover, (B, k + 1), "u_recover")
+        hits = out.get("cache_hit")
         self.forks = SvForks(int(f), out["fork_tokens"].data_ptr(),
-                             out["fork_probs"].data_ptr()) if f > 0 else None
+                             out["fork_probs"].data_ptr(),
+                             hits.data_ptr() if hits is not None else None) if f > 0 else None
         buf = workspace.get(workspace_size(B, k, self.batch.V, f),
                             ("verify", B, k, self.batch.V, f), stream)
         self._buf = buf
