@@ -510,11 +510,27 @@ __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, i
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
         const int t = t0 + q * kLanes + lane;
-        // segment holding flat index t; the lane reads happen with every
-        // lane active (a cross-lane read from an inactive lane returns 0)
-        int seg = 0;
-        for (int g = 0; g < np; ++g) seg += (readlane_i(incl, g) <= t) ? 1 : 0;
-        seg = min(seg, np - 1);
+        // segment holding flat index t: the first g < np with incl[g] > t.
+        // Few segments: a scan of lane reads; many (small batches): a
+        // binary search over the lanes' running counts.  The cross-lane
+        // reads run with every lane active (a read from an inactive lane
+        // returns 0).
+        int lo = 0;
+        if (np <= 16) {
+          for (int g = 0; g < np; ++g) lo += (readlane_i(incl, g) <= t) ? 1 : 0;
+        } else {
+          int hi = np;
+#pragma unroll
+          for (int it = 0; it < 7; ++it) {  // np <= 64
+            const int mid = (lo + hi) >> 1;
+            const int v = __shfl(incl, min(mid, kLanes - 1));
+            if (lo < hi) {
+              if (v <= t) lo = mid + 1;
+              else hi = mid;
+            }
+          }
+        }
+        const int seg = min(lo, np - 1);
         const int before = __shfl(incl, seg) - __shfl(mycnt, seg);
         pos[q] = -1;
         if (t < total) pos[q] = P.ws.cpos[(base + seg) * kDumpCap + (t - before)];
