@@ -46,6 +46,9 @@ def parse():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seqs", type=int, default=64,
                     help="sequences of the workload the oracle is timed on")
+    ap.add_argument("--latency-b1", action="store_true",
+                    help="instead of the throughput step: the latency of one sv_verify call "
+                         "on each single-sequence workload (B=1), one JSON line each")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of the logits' size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -157,8 +160,56 @@ def cpu_baseline(w, nseq):
                       f"({rows} rows), one process, {dt:.1f} s"}
 
 
+def latency_b1(steps, warmup):
+    """Microseconds per sv_verify call at B = 1, calls issued back to back
+    (device time per call) on the single-sequence workloads."""
+    import numpy as np
+    import torch
+
+    from verification_sampling_amd import specverify as sv
+    from workloads import CONFIGS, make_workload
+
+    dev = torch.device("cuda", 0)
+    for name in ("tiny_verify", "sync_verify_llama_greedy", "sync_verify_llama_t1",
+                 "ssd_step_llama"):
+        cfg = CONFIGS[name]
+        w = make_workload(cfg)
+
+        def logits(a_):
+            if cfg.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a_).view(np.int16)).view(
+                    torch.bfloat16).to(dev)
+            return torch.from_numpy(a_).to(dev)
+
+        x = [logits(w.target), logits(w.draft)] + [
+            torch.from_numpy(v).to(dev)
+            for v in (w.draft_tokens, w.temperature, w.u_accept, w.u_recover)]
+        B, k, f = cfg.B, cfg.k, cfg.f
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_token": torch.empty(B, dtype=torch.int32, device=dev)}
+        if f:
+            out["fork_tokens"] = torch.empty(B, k + 1, f, dtype=torch.int32, device=dev)
+            out["fork_probs"] = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
+        call = sv.PreparedVerify(*x, f, out, sv.Workspace(dev))
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": name, "B": B, "k": k, "f": f, "V": cfg.V,
+                          "logits": cfg.dtype, "us_per_call": e0.elapsed_time(e1) * 1e3 / steps}),
+              flush=True)
+
+
 def main():
     a = parse()
+    if a.latency_b1:
+        latency_b1(a.steps, a.warmup)
+        return
     if a.traffic_from:
         write_traffic(*a.traffic_from)
         return
