@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--latency-b1", action="store_true",
                     help="instead of the throughput step: the latency of one sv_verify call "
                          "on each single-sequence workload (B=1), one JSON line each")
+    ap.add_argument("--stress", action="store_true",
+                    help="instead of the throughput step: the fp32 stress workload (B=256, "
+                         "mixed temperatures): the verify step with forks, then the full "
+                         "residual distributions at the outcome positions")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of the logits' size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -205,8 +209,64 @@ def latency_b1(steps, warmup):
               flush=True)
 
 
+def stress(steps, warmup):
+    """Throughput on the B=256 fp32 stress workload: sv_verify with forks
+    (rows/s, algorithmic GB/s of the logits), then sv_residual_sample with
+    the full residual distributions at the outcome positions (every row read
+    for the statistics, re-read for the residual sums and again for the
+    normalised write)."""
+    import torch
+
+    from verification_sampling_amd import specverify as sv
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS["stress_mixed_tau_fp32"]
+    w = make_workload(cfg)
+    dev = torch.device("cuda", 0)
+    T, D, d, tau, ua, ur = (torch.from_numpy(v).to(dev) for v in (
+        w.target, w.draft, w.draft_tokens, w.temperature, w.u_accept, w.u_recover))
+    B, k, f, V = cfg.B, cfg.k, cfg.f, cfg.V
+    out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "out_token": torch.empty(B, dtype=torch.int32, device=dev),
+           "fork_tokens": torch.empty(B, k + 1, f, dtype=torch.int32, device=dev),
+           "fork_probs": torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)}
+    call = sv.PreparedVerify(T, D, d, tau, ua, ur, f, out, sv.Workspace(dev))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    rows = B * (k + 1)
+    logits = 2 * rows * V * 4
+    t = timed(call, steps)
+    print(json.dumps({"workload": "stress_mixed_tau_fp32", "call": "sv_verify (f=3)",
+                      "us_per_call": t * 1e6, "rows_per_s": rows / t,
+                      "logits_GBs": logits / t / 1e9}), flush=True)
+    pos = out["accept_len"].clone()
+    ws = sv.Workspace(dev)
+    t2 = timed(lambda: sv.residual_sample(T, D, d, tau, pos, ur, want_residual=True,
+                                          workspace=ws), max(1, steps // 4))
+    alg = logits + rows * V * 4
+    print(json.dumps({"workload": "stress_mixed_tau_fp32",
+                      "call": "sv_residual_sample (full distributions)",
+                      "us_per_call": t2 * 1e6, "alg_bytes": alg, "alg_GBs": alg / t2 / 1e9,
+                      "moved_bytes": 3 * logits + rows * V * 4,
+                      "moved_GBs": (3 * logits + rows * V * 4) / t2 / 1e9}), flush=True)
+
+
 def main():
     a = parse()
+    if a.stress:
+        stress(a.steps, a.warmup)
+        return
     if a.latency_b1:
         latency_b1(a.steps, a.warmup)
         return
