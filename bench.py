@@ -151,17 +151,45 @@ def write_traffic(fetch_csv, write_csv):
 
 
 def cpu_baseline(w, nseq):
+    """The oracle timed on the first nseq sequences; returns the baseline
+    record and the oracle's result (for the parity check)."""
     import oracle
 
     seqs = list(range(min(nseq, w.B)))
     t0 = time.perf_counter()
-    oracle.verify_batch(w.target, w.draft, w.dtype, w.draft_tokens, w.temperature,
-                        w.u_accept, w.u_recover, f=w.f, seqs=seqs)
+    ref = oracle.verify_batch(w.target, w.draft, w.dtype, w.draft_tokens, w.temperature,
+                              w.u_accept, w.u_recover, f=w.f, seqs=seqs)
     dt = time.perf_counter() - t0
     rows = len(seqs) * (w.k + 1)
     return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(seqs)} of {w.B} sequences of {WORKLOAD} "
-                      f"({rows} rows), one process, {dt:.1f} s"}
+                      f"({rows} rows), one process, {dt:.1f} s"}, ref
+
+
+def parity(out, ref):
+    """The timed calls' outputs (input set 0, the workload in its own order)
+    against the oracle on the same sequences: token ids, accepted lengths and
+    fork tokens bit-exact on every sequence the oracle does not flag (a
+    uniform within 1e-6 of a decision boundary), fork probabilities within
+    1e-5 relative."""
+    import numpy as np
+
+    seqs = np.asarray(ref.seqs)
+    al = out["accept_len"].cpu().numpy()[seqs]
+    tok = out["out_token"].cpu().numpy()[seqs]
+    ft = out["fork_tokens"].cpu().numpy()[seqs]
+    fp = out["fork_probs"].cpu().numpy()[seqs].astype(np.float64)
+    bad = 0
+    for i in range(len(seqs)):
+        if ref.flagged[i]:
+            continue
+        if al[i] != ref.accept_len[i] or tok[i] != ref.token[i]:
+            bad += 1
+    fork_bad = int(np.sum(np.any(ft != ref.fork_tokens, axis=(1, 2))))
+    prob_bad = int(np.sum(np.abs(fp - ref.fork_probs) > 1e-5 * np.abs(ref.fork_probs) + 1e-30))
+    return {"sequences": int(len(seqs)), "flagged_sequences": int(np.sum(ref.flagged)),
+            "flagged_draws": int(ref.n_flagged_draws), "token_or_length_mismatches": bad,
+            "fork_token_mismatches": fork_bad, "fork_probs_outside_1e-5": prob_bad}
 
 
 def latency_b1(steps, warmup):
@@ -304,7 +332,7 @@ def main():
         sets.append({key: torch.roll(v, r, 0).contiguous() for key, v in base.items()})
     del base
     ws = sv.Workspace(dev)
-    calls = []
+    calls, outs = [], []
     for s in sets:
         out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
                "out_token": torch.empty(B, dtype=torch.int32, device=dev),
@@ -312,6 +340,7 @@ def main():
                "fork_probs": torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)}
         calls.append(sv.PreparedVerify(s["T"], s["D"], s["d"], s["tau"], s["ua"], s["ur"],
                                        f, out, ws))
+        outs.append(out)
     torch.cuda.synchronize()
 
     hip = Hip()
@@ -383,7 +412,8 @@ def main():
         "step_frac_of_hbm_peak": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seqs)
+        res["cpu_baseline"], ref = cpu_baseline(w, a.cpu_seqs)
+        res["parity"] = parity(outs[0], ref)
     print(json.dumps(res), flush=True)
 
 
