@@ -236,6 +236,37 @@ def test_forked_topf_standalone(sv, f):
     log(f"[edges] forked_topf f={f}: ok")
 
 
+def test_cache_hit_on_drafter_forks(sv):
+    """SSD placement: the drafter ranks its forks with sv_forked_topf, the
+    verifier decides without forks, and sv_cache_hit looks the outcome up in
+    the drafter's forks.  The hits equal the oracle's lookup of its own
+    outcome in its own forks on every unflagged sequence, and the fused
+    lookup of a verify call with forks."""
+    B, k, V, f = 24, 7, 6000, 3
+    w = synth(B, k, V, "bf16", 0.8, seed=77)
+    tau = w.temperature.copy()
+    tau[::5] = 0.0
+    D = padded_dev(w.draft, "bf16")
+    T = padded_dev(w.target, "bf16")
+    d = torch.from_numpy(w.draft_tokens).cuda()
+    tt = torch.from_numpy(tau).cuda()
+    ua, ur = torch.from_numpy(w.u_accept).cuda(), torch.from_numpy(w.u_recover).cuda()
+    toks, _ = sv.forked_topf(D, d, tt, f)
+    out = sv.verify(T, D, d, tt, ua, ur)
+    hits = sv.cache_hit(toks, out["accept_len"], out["out_token"])
+    fused = sv.verify(T, D, d, tt, ua, ur, f=f, want_hits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hits, fused["cache_hit"])
+    ref = oracle.verify_batch(w.target, w.draft, "bf16", w.draft_tokens, tau, w.u_accept,
+                              w.u_recover, f=f)
+    ref_hits = oracle.cache_hits_batch(ref.fork_tokens, ref.accept_len, ref.token)
+    h = hits.cpu().numpy()
+    for b in range(B):
+        if not ref.flagged[b]:
+            assert h[b] == ref_hits[b], (b, int(h[b]), int(ref_hits[b]))
+    log(f"[edges] cache hits on drafter forks: {int((h >= 0).sum())}/{B}")
+
+
 def test_workspace_reused_across_shapes(sv):
     """One workspace serves calls of different sizes and entry points in
     turn: the arrival counters move with the sizes, and every call must find
