@@ -98,6 +98,7 @@ struct Params {
   int32_t nslab;           // slabs per row
   int32_t nparts;          // k_stats segments (partials) per row
   int32_t nbs;             // k_decide blocks per task row
+  int32_t fsplit;          // k_decide fork blocks per sequence
   int64_t nslots;          // row slots of k_stats
   int64_t rows_per_temp;   // softmax
   int32_t* accept_len;
@@ -827,6 +828,8 @@ struct DecideLds {
   RowStat rs[kMaxK + 1];
   float hv[kMaxK + 1][2][kMaxF];  // fork blocks: each half's top-f per row
   int hi[kMaxK + 1][2][kMaxF];
+  float wv[kDecideWaves][kMaxF];  // split fork blocks: each wave's top-f
+  int wi[kDecideWaves][kMaxF];
   int n, status;
 };
 
@@ -1089,6 +1092,65 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const int lane = lane_id();
   const int K1 = P.k + 1;
   const int64_t ntasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * K1 : P.B;
+  if ((int64_t)blockIdx.x >= ntasks * P.nbs && P.fsplit > 1) {
+    // a split fork block (small batches): fork block r of the sequence ranks
+    // rows r, r + fsplit, ... with nsplit waves each, after a merge-only
+    // pass over every row that gives the decision its validity flags
+    const int fb = (int)(blockIdx.x - ntasks * P.nbs);
+    const int b = fb / P.fsplit;
+    const int r0 = fb - b * P.fsplit;
+    const float tau = P.tau[b];
+    if (!(tau > 0.0f && tau_ok(tau))) return;  // the owner block ranks these
+    SeqIn sin;
+    if (w == 0) sin = load_seq_inputs(P, b);
+    for (int j = w; j < K1; j += kDecideWaves) row_stat<In, F>(P, b, j, tau, &S.rs[j], false);
+    __syncthreads();
+    const int rpb = (K1 - r0 + P.fsplit - 1) / P.fsplit;  // rows of this block, >= 1
+    const int nsplit = min(kDecideWaves / rpb, kLanes / P.f);
+    if (w < rpb * nsplit) {
+      const int jj = w % rpb, h = w / rpb;
+      const int j = r0 + jj * P.fsplit;
+      row_stat<In, F>(P, b, j, tau, &S.rs[j], true, h, nsplit, S.wv[w], S.wi[w]);
+    }
+    __syncthreads();
+    if (w == 0) {
+      int n, status;
+      decide_sequence(P, b, S, sin, false, n, status);
+      if (lane == 0) S.status = status;
+    }
+    __syncthreads();
+    if (S.status == 0) return;
+    if constexpr (F > 0) {
+      if (w < rpb) {
+        // the row's nsplit lists merged (lane h * f + r holds entry r of
+        // the list of wave h * rpb + w)
+        const int j = r0 + w * P.fsplit;
+        TopList<F> l, top;
+        l.clear();
+        if (lane < nsplit * P.f) {
+          const int h = lane / P.f, r = lane - h * P.f;
+          l.insert(S.wv[h * rpb + w][r], S.wi[h * rpb + w][r]);
+        }
+        wave_merge_lists<F>(l, P.f, top);
+        const float qm = S.rs[j].qm;
+        const double qs = S.rs[j].qs;
+        const double cd = (double)scale_of(tau);
+#pragma unroll
+        for (int r = 0; r < F; ++r) {
+          if (lane == r && r < P.f) {
+            const float v = top.v[r];
+            const float prob = (!finitef(qm) || !(v > neg_inf()))
+                                   ? 0.0f
+                                   : (float)(exp2(((double)v - (double)qm) * cd) / qs);
+            const int64_t o = ((int64_t)b * K1 + j) * P.f + r;
+            P.fork_tok[o] = top.i[r];
+            if (P.fork_prob) P.fork_prob[o] = prob;
+          }
+        }
+      }
+    }
+    return;
+  }
   if ((int64_t)blockIdx.x >= ntasks * P.nbs) {
     // a fork block: the forks of one sequence at temperature > 0, ranked
     // beside the blocks that sum and draw
@@ -1633,7 +1695,15 @@ template <typename In, int F>
 static hipError_t launch_decide_F(Params P, hipStream_t s) {
   const int64_t tasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
   if (tasks == 0) return hipSuccess;
-  const int64_t fork_blocks = (P.mode == kVerify && P.fork_tok) ? P.B : 0;
+  // fork blocks per sequence: one, or (small batches, k + 1 <= 16) up to one
+  // per row while they take at most a quarter of the CUs
+  const bool forks = P.mode == kVerify && P.fork_tok;
+  int fsplit = 1;
+  if (forks && P.k + 1 <= kDecideWaves) {
+    while (fsplit * 2 <= P.k + 1 && (int64_t)P.B * fsplit * 2 <= device_cus() / 4) fsplit *= 2;
+  }
+  P.fsplit = fsplit;
+  const int64_t fork_blocks = forks ? (int64_t)P.B * fsplit : 0;
   int64_t nbs = (device_cus() - fork_blocks) / tasks;
   nbs = std::max<int64_t>(1, std::min<int64_t>(nbs, std::max<int64_t>(1, P.cpr / 8)));
   P.nbs = (int32_t)nbs;
