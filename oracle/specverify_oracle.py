@@ -59,6 +59,9 @@ bonus token from ``p_k``.  Readings of the points the pages leave open:
    outside [0, V), or a logits row that is read and whose maximum is not
    finite (+inf, or every entry -inf) make the whole sequence an error.
    NaN logits are outside the contract (this oracle raises).
+10. Speculation-cache lookup: the outcome (n, token) hits when the token is
+   one of the f forks at position n, and the hit is its index there; an
+   error outcome never hits.
 """
 
 from __future__ import annotations
