@@ -12,7 +12,8 @@ from .specverify_oracle import (BF16, F32, FLAG_BAND, BatchResult, ProbVerdict,
                                 first_rejection, forked_topf,
                                 forked_topf_batch, inverse_cdf,
                                 residual_distribution, residual_weights,
-                                sample_at_position, softmax_rows,
+                                sample_at_position, sample_rows, sample_temp,
+                                softmax_rows,
                                 softmax_temp, verify_batch, verify_from_probs,
                                 verify_greedy, verify_sequence, widen)
 
@@ -21,6 +22,7 @@ __all__ = ["BF16", "F32", "FLAG_BAND", "BatchResult", "ProbVerdict",
            "argmax_first", "cache_hit", "cache_hits_batch",
            "first_rejection", "forked_topf",
            "forked_topf_batch", "inverse_cdf", "residual_distribution",
-           "residual_weights", "sample_at_position", "softmax_rows",
+           "residual_weights", "sample_at_position", "sample_rows",
+           "sample_temp", "softmax_rows",
            "softmax_temp", "verify_batch", "verify_from_probs",
            "verify_greedy", "verify_sequence", "widen"]

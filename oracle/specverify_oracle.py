@@ -533,3 +533,40 @@ def cache_hits_batch(fork_tokens, accept_len, token) -> np.ndarray:
         if 0 <= n < K1 and t >= 0:
             out[b] = cache_hit(fork_tokens[b, n], t)
     return out
+
+
+def sample_temp(x, tau: float, u):
+    """The drafter's own draw from one logits row: greedy at temperature 0,
+    stochastic above it.
+
+    [SSD-summary], the highlighted sampler file: sampling is greedy or
+    stochastic according to the temperature.  At tau = 0 the token is the
+    lowest id holding the maximum; above it, the inverse-CDF draw (reading 4)
+    from softmax(x / tau) with the uniform u.  Returns (token, flagged); a
+    row whose maximum is not finite, or an invalid temperature, raises
+    RowError.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not _tau_ok(float(tau)):
+        raise RowError("temperature")
+    _check_row(x)
+    if tau == 0.0:
+        return argmax_first(x), False
+    return inverse_cdf(softmax_temp(x, tau).tolist(), float(u))
+
+
+def sample_rows(logits, dtype, temperatures, uniforms):
+    """sample_temp over the rows of a [rows, V] array (one temperature and
+    one uniform per row): (tokens [rows], flagged [rows]); error rows get
+    -1."""
+    logits = np.asarray(logits)
+    R = logits.shape[0]
+    toks = np.full(R, -1, dtype=np.int64)
+    flags = np.zeros(R, dtype=bool)
+    for r in range(R):
+        try:
+            toks[r], flags[r] = sample_temp(widen(logits[r], dtype), float(temperatures[r]),
+                                            float(uniforms[r]))
+        except RowError:
+            pass
+    return toks, flags

@@ -362,3 +362,44 @@ def test_cache_hit_invariants_on_synthetic_batches(tau):
             assert r.token[i] not in list(r.fork_tokens[i, n])
         if n < w.k:
             assert w.draft_tokens[i, n] not in list(r.fork_tokens[i, n])
+
+
+# ---------------------------------------------------------------- drafter draw
+
+def test_hand_worked_sample_temp():
+    """p = (1/2, 1/4, 1/4) at tau = 1: running sums (1/2, 3/4, 1), so u in
+    [0, 1/2) draws 0, [1/2, 3/4) draws 1, [3/4, 1) draws 2."""
+    x = np.log([0.5, 0.25, 0.25])
+    for u, want in ((0.0, 0), (0.49, 0), (0.51, 1), (0.74, 1), (0.76, 2), (0.999, 2)):
+        assert oracle.sample_temp(x, 1.0, u)[0] == want, u
+    assert oracle.sample_temp(x, 1.0, 0.5)[1]          # on a breakpoint: flagged
+    assert oracle.sample_temp([1.0, 3.0, 3.0, 2.0], 0.0, 0.9) == (1, False)  # greedy, lowest tied id
+
+
+def test_sample_temp_law_is_the_softmax():
+    """Over a lattice of 20000 uniforms the draws follow softmax(x / tau)
+    (scipy) to within the lattice resolution."""
+    rng = np.random.default_rng(3)
+    for tau in (0.5, 1.0, 1.7):
+        x = rng.normal(0, 1.5, 7)
+        p = scipy.special.softmax(x / tau)
+        L = 20000
+        counts = np.zeros(7)
+        for i in range(L):
+            counts[oracle.sample_temp(x, tau, (i + 0.5) / L)[0]] += 1
+        np.testing.assert_allclose(counts / L, p, atol=2.0 / L)
+
+
+def test_sample_temp_scaling_and_errors():
+    """Drawing from x at tau equals drawing from x / tau at tau = 1; rows
+    without a finite maximum, and invalid temperatures, are errors."""
+    rng = np.random.default_rng(8)
+    x = rng.normal(0, 2, 50)
+    for u in rng.random(40):
+        a, fa = oracle.sample_temp(x, 0.4, u)
+        b, fb = oracle.sample_temp(x / 0.4, 1.0, u)
+        if not (fa or fb):
+            assert a == b
+    toks, flags = oracle.sample_rows(np.stack([x, np.full(50, -np.inf), x]), "f32",
+                                     [1.0, 1.0, -1.0], [0.3, 0.3, 0.3])
+    assert toks[1] == -1 and toks[2] == -1 and toks[0] >= 0
