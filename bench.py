@@ -53,6 +53,9 @@ def parse():
                     help="instead of the throughput step: the fp32 stress workload (B=256, "
                          "mixed temperatures): the verify step with forks, then the full "
                          "residual distributions at the outcome positions")
+    ap.add_argument("--sample", action="store_true",
+                    help="instead of the throughput step: the drafter's draw (sv_sample_temp) "
+                         "on the 512 draft rows of the batched workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of the logits' size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -290,8 +293,45 @@ def stress(steps, warmup):
                       "moved_GBs": (3 * logits + rows * V * 4) / t2 / 1e9}), flush=True)
 
 
+def sample_rows(steps, warmup):
+    """sv_sample_temp on the 512 draft rows of the batched Qwen3-vocabulary
+    workload (one uniform per row, the workload's temperatures): rows/s and
+    algorithmic GB/s (each row read once)."""
+    import numpy as np
+    import torch
+
+    from verification_sampling_amd import specverify as sv
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[WORKLOAD]
+    w = make_workload(cfg)
+    dev = torch.device("cuda", 0)
+    B, k, V = cfg.B, cfg.k, cfg.V
+    rows = B * (k + 1)
+    x = torch.from_numpy(np.ascontiguousarray(w.draft).view(np.int16)).view(
+        torch.bfloat16).reshape(rows, V).to(dev)
+    tau = torch.from_numpy(w.temperature).to(dev)
+    u = torch.from_numpy(np.ascontiguousarray(w.u_recover.reshape(-1))).to(dev)
+    for _ in range(warmup):
+        sv.sample_temp(x, tau, u, rows_per_temp=k + 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sv.sample_temp(x, tau, u, rows_per_temp=k + 1)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    print(json.dumps({"workload": WORKLOAD + " draft rows", "call": "sv_sample_temp",
+                      "rows": rows, "us_per_call": t * 1e6, "rows_per_s": rows / t,
+                      "alg_GBs": rows * V * 2 / t / 1e9}), flush=True)
+
+
 def main():
     a = parse()
+    if a.sample:
+        sample_rows(a.steps, a.warmup)
+        return
     if a.stress:
         stress(a.steps, a.warmup)
         return

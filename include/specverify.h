@@ -225,6 +225,27 @@ sv_status sv_cache_hit(int32_t B, int32_t k, int32_t f,
                        const int32_t* fork_tokens, const int32_t* accept_len,
                        const int32_t* out_token, int32_t* hits, void* stream);
 
+/* The drafter's own draw from its logits rows: greedy or stochastic by
+ * temperature (tanishqkumar/ssd repository summary, highlighted sampler
+ * file).  tokens[r] = the lowest id holding the maximum of row r when its
+ * temperature is 0; otherwise the inverse-CDF draw from softmax(row / tau)
+ * with the uniform uniforms[r]: the first token, in id order, whose running
+ * sum of probabilities exceeds the uniform (the last token of positive
+ * probability if rounding leaves none).
+ *   logits       rows of V elements (dtype) at row_stride elements; rows
+ *                16-byte aligned; V <= 1048576 (fp32) / 2097152 (bf16)
+ *   temperature  [ceil(rows / rows_per_temp)] fp32: row r uses
+ *                temperature[r / rows_per_temp]
+ *   uniforms     [rows] fp32 in [0, 1)
+ *   tokens       [rows] int32 out; -1 for a row whose maximum is not finite
+ *                or whose temperature is NaN, negative or infinite.
+ * One block per row reads the row once (plus one 1-2 KiB slab of it for
+ * the draw); no workspace. */
+sv_status sv_sample_temp(const void* logits, int32_t dtype, int64_t rows,
+                         int32_t V, int64_t row_stride,
+                         const float* temperature, int64_t rows_per_temp,
+                         const float* uniforms, int32_t* tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -143,3 +143,23 @@ def test_cache_hit_validation(L):
         args = [p, p, p, p]
         args[i] = None
         assert L.sv_cache_hit(4, 7, 3, *args, None) == INVALID
+
+
+def test_sample_temp_validation(L):
+    p = ctypes.c_void_p(FAKE)
+
+    def call(logits=p, dtype=1, rows=4, V=1000, stride=1000, temp=p, rpt=1, u=p, out=p):
+        return L.sv_sample_temp(logits, dtype, rows, V, stride, temp, rpt, u, out, None)
+
+    assert call(rows=0, logits=None, temp=None, u=None, out=None) == OK
+    assert call(rows=-1) == INVALID
+    assert call(V=1) == INVALID
+    assert call(dtype=2) == INVALID
+    assert call(rpt=0) == INVALID
+    assert call(stride=999) == INVALID
+    assert call(dtype=0, V=1048577, stride=1048580) == INVALID    # more than 4096 fp32 slabs
+    assert call(V=2097153, stride=2097160) == INVALID             # more than 4096 bf16 slabs
+    assert call(stride=1004) == MISALIGNED                         # bf16 rows of 2008 bytes
+    assert call(logits=ctypes.c_void_p(FAKE + 8)) == MISALIGNED
+    for name in ("logits", "temp", "u", "out"):
+        assert call(**{name: None}) == INVALID

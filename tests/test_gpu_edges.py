@@ -292,3 +292,33 @@ def test_workspace_reused_across_shapes(sv):
             torch.cuda.synchronize()
             assert torch.equal(toks, out["fork_tokens"])
     log("[edges] workspace reused across shapes and entry points: ok")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sample_temp_rows(sv, dtype):
+    """The drafter's draw on logits rows of several vocabularies (ragged
+    tails, one and many slabs), temperatures 0 and above, and error rows,
+    against the oracle: tokens equal on every row it does not flag."""
+    rng = np.random.default_rng(31 if dtype == "bf16" else 32)
+    for V in (2, 7, 1000, 4097, 128256):
+        w = synth(2, 7, V, dtype, 0.8, seed=900 + V)
+        rows = w.draft.reshape(-1, V)              # 16 rows
+        R = rows.shape[0]
+        tau = np.where(rng.random(R) < 0.25, 0.0, rng.uniform(0.3, 1.5, R)).astype(np.float32)
+        u = uniforms(rng, (R,))
+        host = rows.copy()
+        if V > 2:
+            tau[3] = -1.0                          # invalid temperature
+            if dtype == "bf16":
+                host[5] = f32_to_bf16_bits(np.full(V, -np.inf, dtype=np.float32))
+            else:
+                host[5] = -np.inf                  # no finite entry
+        x = padded_dev(host[None], dtype)[0]
+        got = sv.sample_temp(x, torch.from_numpy(tau).cuda(), torch.from_numpy(u).cuda())
+        torch.cuda.synchronize()
+        ref, flagged = oracle.sample_rows(host, dtype, tau, u)
+        g = got.cpu().numpy()
+        for r in range(R):
+            if not flagged[r]:
+                assert g[r] == ref[r], (V, r, int(g[r]), int(ref[r]), float(tau[r]))
+        log(f"[edges] sample_temp {dtype} V={V}: {int((~flagged).sum())}/{R} rows compared")

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 
-SOURCES = [os.path.join(CSRC, "specverify.hip")]
+SOURCES = [os.path.join(CSRC, "specverify.hip"), os.path.join(CSRC, "sv_sample.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

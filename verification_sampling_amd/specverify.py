@@ -87,6 +87,8 @@ def lib():
             L.sv_forked_topf.restype = i32
             L.sv_cache_hit.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
             L.sv_cache_hit.restype = i32
+            L.sv_sample_temp.argtypes = [vp, i32, i64, i32, i64, vp, i64, vp, vp, vp]
+            L.sv_sample_temp.restype = i32
             _lib = L
     return _lib
 
@@ -311,6 +313,27 @@ def cache_hit(fork_tokens, accept_len, out_token, stream=None):
                               _ptr(out_token), _ptr(hits), _stream_handle(stream))
     _check(code, "sv_cache_hit")
     return hits
+
+
+def sample_temp(logits, temperature, uniforms, rows_per_temp: int = 1, stream=None):
+    """sv_sample_temp: one token per row of a [rows, V] tensor (V
+    contiguous): greedy at temperature 0, else the inverse-CDF draw from
+    softmax(row / tau) with that row's uniform.  Returns int32 [rows] (-1
+    for an error row)."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, V] with V contiguous")
+    rows, V = logits.shape
+    if temperature.dtype != torch.float32 or not temperature.is_contiguous():
+        raise ValueError("temperature must be contiguous float32")
+    if (temperature.numel() * rows_per_temp < rows):
+        raise ValueError("one temperature per rows_per_temp rows is needed")
+    _f32(uniforms, (rows,), "uniforms")
+    toks = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    code = lib().sv_sample_temp(_ptr(logits), _dtype_code(logits), int(rows), int(V),
+                                logits.stride(0), _ptr(temperature), int(rows_per_temp),
+                                _ptr(uniforms), _ptr(toks), _stream_handle(stream))
+    _check(code, "sv_sample_temp")
+    return toks
 
 
 def softmax_temp(logits, temperature, rows_per_temp: int = 1,
