@@ -1,23 +1,28 @@
 // libspecverify: kernels and the C ABI entry points (gfx950).
 //
-// Kernel chain of sv_verify (one stream, no host synchronisation, no
-// device-scope atomics):
+// Kernel chain of sv_verify (one stream, no host synchronisation):
 //   k_stats   one round of resident waves; each streams one segment of
 //             consecutive slabs of one row (target and draft together,
-//             16-byte loads, the next chunk in flight while the current one
-//             is folded) and writes the segment's partial statistics: row
-//             reference, fp64 sum of exponentials, argmax at temperature 0,
-//             and the draft's top-F fork candidates with the drafted token
-//             masked out.
-//   k_decide  one 1024-thread block per sequence: its waves merge the rows'
-//             partials in LDS (row reference and sum, argmax, p(d), q(d),
-//             forks); wave 0 runs the acceptance tests and finds the first
-//             rejection by ballot; the outputs are written; for temperature
-//             > 0 the block re-reads row n, sums max(0, p - q) (or p) per
-//             chunk, and wave 0 draws the token by inverse CDF.
-// sv_residual_sample runs the same pair at given positions (plus k_write for
-// the full residual distributions); sv_softmax_temp runs k_stats then
-// k_write; sv_forked_topf runs k_stats then k_decide without draws.
+//             non-temporal 16-byte loads, the next chunk in flight while the
+//             current one is folded) and writes the segment's partial
+//             statistics: row reference, fp64 sum of exponentials, argmax at
+//             temperature 0, and the draft's fork candidates with the
+//             drafted token masked out.  No atomics.
+//   k_decide  1024-thread blocks, several per sequence: each merges the
+//             rows' partials in LDS (row reference and sum, argmax, p(d),
+//             q(d)); wave 0 runs the acceptance tests and finds the first
+//             rejection by ballot; the owner block writes the outputs; for
+//             temperature > 0 the blocks split row n, sum max(0, p - q) (or
+//             p) per chunk, hand the chunk totals to the last to arrive
+//             (device-scope stores and one arrival counter per sequence),
+//             and that block draws the token by inverse CDF.  Fork blocks
+//             (one per sequence, or one per few rows at small batches) rank
+//             the fork candidates beside them.
+//   k_hits    (forks->hits) the speculation-cache lookup of the outcome.
+// sv_residual_sample runs k_stats and k_decide at given positions (plus
+// k_write for the full residual distributions); sv_softmax_temp runs
+// k_stats then k_write; sv_forked_topf runs k_stats then k_decide without
+// draws; sv_cache_hit runs k_hits alone.
 //
 // The speculative-sampling rule (accept iff u < min(1, p/q), first
 // rejection, draw from max(0, p - q), bonus draw from p_k) follows the
@@ -1226,7 +1231,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
 
   // 1. row statistics, one wave per row.  Forks are ranked here by the
   // owner at temperature 0 (the greedy q(d) needs the draft's top-1) and for
-  // the forks-only call; at temperature > 0 a fork block of their own does.
+  // the forks-only call; at temperature > 0 fork blocks of their own do.
   const bool forks_now = owner && (P.mode == kForks || !(tau > 0.0f && tau_ok(tau)));
   SeqIn sin;
   if (w == 0) sin = load_seq_inputs(P, b);
@@ -1689,8 +1694,9 @@ static hipError_t launch_stats_F(Params& P, hipStream_t s) {
 }
 
 // k_decide: enough blocks per task row to cover the device (one 1024-thread
-// block per CU), at least eight chunks of the summed row per block, plus one
-// fork block per sequence when verify asks for forks.
+// block per CU), at least eight chunks of the summed row per block, plus the
+// fork blocks when verify asks for forks (one per sequence, or up to one per
+// row at small batches).
 template <typename In, int F>
 static hipError_t launch_decide_F(Params P, hipStream_t s) {
   const int64_t tasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
