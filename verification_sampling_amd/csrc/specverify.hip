@@ -160,6 +160,7 @@ struct RowPlan {
   bool pos_ok, readT, readD, topf, greedy, tok;
   int mask_id;  // element left out of the draft's masked statistics (-1: none)
   int d_id;     // the drafted token of the row (-1: none)
+  int nf;       // forks asked for (f <= F)
 };
 
 __device__ __forceinline__ RowPlan plan_row(const Params& P, int b, int j, float tau) {
@@ -177,6 +178,7 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int b, int j, float
   else r.readD = false;
   r.mask_id = -1;
   r.d_id = -1;
+  r.nf = P.f;
   if (r.pos_ok && j < P.k && P.mode != kSoftmax) {
     const int d = P.drafts[(int64_t)b * P.k + j];
     r.d_id = d;  // out-of-range ids match no element
@@ -278,12 +280,13 @@ __device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* 
       if (pl.topf) {
         unsigned bits = 0;
         if constexpr (FIRST) {
-          // every element of the chunk's top-F reaches the F-th largest lane
-          // maximum; the first chunk's candidates are the vectors there
+          // at least f vectors reach the f-th largest lane maximum, so every
+          // element of the segment's top-f does; the first chunk's
+          // candidates are the vectors there
           float lm = m8[0];
 #pragma unroll
           for (int u = 1; u < kU; ++u) lm = fmaxf(lm, m8[u]);
-          st.kv = wave_fth_largest<F>(lm, F);
+          st.kv = wave_fth_largest<F>(lm, pl.nf);
 #pragma unroll
           for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
         } else if (!(st.kv > neg_inf())) {
@@ -494,9 +497,9 @@ __device__ __forceinline__ Merged merge_lanes(float mi, double si, int ai, bool 
 // The candidate vectors the segments of row (b, j) passed on (cnt: this
 // lane's segment's count, lanes < np): positions, then vectors, are loaded
 // a round of 64 * kRound at a time; their elements (id < V, id != mask_id)
-// at or above the F-th largest of the lanes' maxima over the loaded
+// at or above the f-th largest of the lanes' maxima over the loaded
 // vectors go into this lane's list.  That bound never drops one of the
-// row's top-F: at least F of the loaded elements reach it.  With nhalf = 2,
+// row's top-f: at least f of the loaded elements reach it.  With nhalf = 2,
 // two waves share the row: wave `half` takes every other round.
 template <typename In, int F>
 __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, int64_t base,
@@ -561,7 +564,7 @@ __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, i
       // a lane with an element at -inf still counts towards the F
       const float key = any ? lm : neg_inf();
       const unsigned long long have = __ballot(any);
-      const float kvr = (__popcll(have) >= F) ? wave_fth_largest<F>(key, F) : neg_inf();
+      const float kvr = (__popcll(have) >= P.f) ? wave_fth_largest<F>(key, P.f) : neg_inf();
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
         float thr = fmaxf(kvr, mine.v[F - 1]);
