@@ -403,3 +403,144 @@ def test_sample_temp_scaling_and_errors():
     toks, flags = oracle.sample_rows(np.stack([x, np.full(50, -np.inf), x]), "f32",
                                      [1.0, 1.0, -1.0], [0.3, 0.3, 0.3])
     assert toks[1] == -1 and toks[2] == -1 and toks[0] >= 0
+
+
+# ---------------------------------------------------------------- flags
+#
+# A draw whose uniform lies within 1e-6 of a decision boundary is flagged
+# and its sequence left out of the bit-exact comparison.  The band, and the
+# rule that only tests up to the first rejection n count, are pinned here on
+# hand-built distributions whose acceptance probabilities are exact binary
+# fractions (so |u - a| is known without rounding).
+
+def _one_position(p_d, q_d, u, d=1):
+    """k = 1, V = 2: p0 and q0 put p_d / q_d on token d; the bonus row is
+    uniform.  Returns the verdict."""
+    P0 = [1 - p_d, p_d] if d == 1 else [p_d, 1 - p_d]
+    Q0 = [1 - q_d, q_d] if d == 1 else [q_d, 1 - q_d]
+    return oracle.verify_from_probs([P0, [0.5, 0.5]], [Q0], [d], [u], [0.3, 0.3])
+
+
+@pytest.mark.parametrize("delta,flagged", [(5e-7, True), (-5e-7, True), (9.9e-7, True),
+                                           (2e-6, False), (-2e-6, False), (1.1e-6, False)])
+def test_acceptance_flag_band(delta, flagged):
+    """a = p/q = 0.25/0.5 = 1/2 exactly; u = 1/2 + delta."""
+    v = _one_position(0.25, 0.5, 0.5 + delta)
+    assert v.accept_flags == [flagged]
+    assert v.flagged == flagged
+    # the decision itself is u < a
+    assert v.accept_len == (1 if delta < 0 else 0)
+
+
+def test_acceptance_flag_band_at_a_equal_one():
+    """p > q gives a = 1: only u within 1e-6 of 1 is flagged; u = 0 (the
+    other end of [0, 1)) is not, and u = 0 is always accepted."""
+    assert _one_position(0.75, 0.5, 1 - 2**-24).accept_flags == [True]
+    assert _one_position(0.75, 0.5, 1 - 2**-17).accept_flags == [False]
+    v = _one_position(0.75, 0.5, 0.0)
+    assert v.accept_flags == [False] and v.accept_len == 1
+
+
+def test_acceptance_flag_band_q_zero_and_p_zero():
+    """q(d) = 0 < p(d): a = 1; p(d) = 0: a = 0, so u = 0 is rejected and
+    flagged (|0 - 0| < 1e-6), u = 2^-24 rejected and flagged, u = 2^-19
+    rejected and not flagged."""
+    v = _one_position(0.5, 0.0, 0.5)
+    assert v.accept_len == 1 and not v.flagged
+    v = _one_position(0.0, 0.5, 0.0)
+    assert v.accept_len == 0 and v.accept_flags == [True] and v.flagged
+    assert _one_position(0.0, 0.5, 2**-24).flagged
+    v = _one_position(0.0, 0.5, 2**-19)
+    assert v.accept_len == 0 and not v.flagged
+
+
+def _three_positions(u_acc):
+    """k = 3, V = 2, drafted token 1 everywhere, a_j = 1/2 at every
+    position (p = 1/4, q = 1/2).  Residual at a rejection: (1/4, 0) ->
+    token 0; bonus row (1/2, 1/2)."""
+    P = [[0.75, 0.25]] * 3 + [[0.5, 0.5]]
+    Q = [[0.5, 0.5]] * 3
+    return oracle.verify_from_probs(P, Q, [1, 1, 1], u_acc, [0.3] * 4)
+
+
+def test_flags_after_the_first_rejection_do_not_count():
+    """Position 0 rejects clearly (u = 0.9 >= 1/2), so n = 0; positions 1
+    and 2 sit inside the band, but a flip there cannot change n: the
+    sequence is not flagged, though their per-position flags are set."""
+    v = _three_positions([0.9, 0.5 + 5e-7, 0.5 - 5e-7])
+    assert v.accept_len == 0
+    assert v.accept_flags == [False, True, True]
+    assert not v.flagged
+
+
+def test_flag_at_or_before_the_first_rejection_counts():
+    # flag at j < n: accepted inside the band, rejected at position 2
+    v = _three_positions([0.5 - 5e-7, 0.1, 0.9])
+    assert v.accept_len == 2 and v.accept_flags == [True, False, False] and v.flagged
+    # flag exactly at j = n: the rejecting test itself is inside the band
+    v = _three_positions([0.1, 0.5 + 5e-7, 0.1])
+    assert v.accept_len == 1 and v.accept_flags == [False, True, False] and v.flagged
+    # every test accepted, the last inside the band (n = k)
+    v = _three_positions([0.1, 0.1, 0.5 - 5e-7])
+    assert v.accept_len == 3 and v.flagged
+    # nothing inside the band
+    v = _three_positions([0.1, 0.5 + 2e-6, 0.5 - 2e-6])
+    assert v.accept_len == 1 and not v.flagged
+
+
+def test_draw_flag_band():
+    """Inverse CDF over (1/2, 1/2): the breakpoint C_0/Z = 1/2.  u = 1/2
+    -/+ 5e-7 picks token 0 / 1, both flagged; 2e-6 away, neither.  A token of
+    weight below 2e-6 Z has both its breakpoints within the band, so drawing
+    it is always flagged."""
+    w = [0.5, 0.5]
+    assert oracle.inverse_cdf(w, 0.5 - 5e-7) == (0, True)
+    assert oracle.inverse_cdf(w, 0.5 + 5e-7) == (1, True)
+    assert oracle.inverse_cdf(w, 0.5 - 2e-6) == (0, False)
+    assert oracle.inverse_cdf(w, 0.5 + 2e-6) == (1, False)
+    tiny = [0.5, 1.5e-6, 0.5]
+    Z = sum(tiny)
+    assert oracle.inverse_cdf(tiny, (0.5 + 0.75e-6) / Z) == (1, True)
+
+
+def test_draw_flag_flags_the_sequence():
+    """A clean acceptance followed by a draw inside the band: the sequence
+    is flagged through its draw flag alone."""
+    P = [[0.75, 0.25], [0.5, 0.5]]
+    Q = [[0.5, 0.5]]
+    v = oracle.verify_from_probs(P, Q, [1], [0.1], [0.3, 0.5 + 5e-7])
+    assert v.accept_len == 1 and v.accept_flags == [False]
+    assert v.draw_flag and v.flagged
+    v = oracle.verify_from_probs(P, Q, [1], [0.1], [0.3, 0.5 + 2e-6])
+    assert not v.draw_flag and not v.flagged
+
+
+def test_batch_flag_counts():
+    """The batch driver's counts, worked by hand on four sequences built from
+    logits with exact probabilities (V = 2, tau = 1): target rows (0, 0)
+    give p = (1/2, 1/2); draft rows (0, ln 3) give q = (1/4, 3/4), so the
+    drafted token 1 has a = (1/2)/(3/4) = 2/3 (up to the rounding of ln 3 and
+    exp, ~1e-16).  k = 2.
+      seq 0: u = (2/3 + 5e-7, 0.1)  rejects at 0 inside the band: flagged, 1 draw
+      seq 1: u = (0.95, 2/3 - 5e-7) rejects at 0; position 1 in the band but
+             after n: not flagged, 0 draws counted
+      seq 2: u = (2/3 - 5e-7, 2/3 + 5e-7) accepted then rejected, both in the
+             band: flagged, 2 draws
+      seq 3: u = (0.1, 0.2)          both accepted (n = k), nothing flagged
+    Every rejection leaves the residual max(0, p - q) = (1/4, 0), whose CDF
+    breakpoints are 0 and 1, and the bonus row p_2 = (1/2, 1/2) has its
+    breakpoint at 1/2: u_recover = 0.3 is far from all of them and picks
+    token 0 in both cases."""
+    k, V = 2, 2
+    T = np.zeros((4, k + 1, V))
+    D = np.zeros((4, k + 1, V))
+    D[:, :, 1] = math.log(3.0)
+    a = 2.0 / 3.0
+    ua = np.array([[a + 5e-7, 0.1], [0.95, a - 5e-7], [a - 5e-7, a + 5e-7], [0.1, 0.2]])
+    ur = np.full((4, k + 1), 0.3)
+    drafts = np.ones((4, k), dtype=np.int64)
+    r = oracle.verify_batch(T, D, "f32", drafts, np.ones(4), ua, ur)
+    np.testing.assert_array_equal(r.accept_len, [0, 0, 1, 2])
+    np.testing.assert_array_equal(r.flagged, [True, False, True, False])
+    assert r.n_flagged_draws == 3
+    np.testing.assert_array_equal(r.token, [0, 0, 0, 0])

@@ -167,20 +167,50 @@ def workspace_size(B: int, k: int, V: int, f: int = 0) -> int:
 
 # ------------------------------------------------------------------ helpers
 
-def _batch(target, draft, draft_tokens, temperature):
+def _same_device(tensors, what):
+    """Every tensor on one ROCm device (checked after the shapes, so that a
+    shape mistake is reported as such whatever the device)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"{what}: all tensors must be on one device, got {sorted(map(str, devs))}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"{what}: tensors must be on a ROCm device, got {dev}")
+    return dev
+
+
+def _batch(target, draft, draft_tokens, temperature, forks: bool = False):
+    """The sv_batch of a call, after checking every shape, dtype and count
+    against the others (a mismatch would make the kernels read outside an
+    allocation).  target: [B, k+1, V] (None for the drafter-side forks);
+    draft: [B, k+1, V], or [B, k, V] when no forks are asked for and a
+    target is given; draft_tokens: [B, k] int32; temperature: [B] float32."""
+    for t, name in ((draft, "draft"), (target, "target")):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError(f"{name} logits must be a 3-D tensor [B, k+1, V]")
+        if t.stride(2) != 1:
+            raise ValueError(f"{name} logits must have V contiguous")
+        _dtype_code(t)
     ref = draft if target is None else target
-    if ref.dim() != 3 or ref.stride(2) != 1:
-        raise ValueError("logits must be [B, k+1, V] with V contiguous")
-    if draft.stride(2) != 1:
-        raise ValueError("draft logits must have V contiguous")
     B, K1, V = ref.shape
-    k = draft_tokens.shape[1]
-    if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
-        raise ValueError("draft_tokens must be contiguous int32 [B, k]")
-    if temperature.dtype != torch.float32 or not temperature.is_contiguous():
-        raise ValueError("temperature must be contiguous float32 [B]")
+    if K1 < 2:
+        raise ValueError("logits need k+1 >= 2 positions")
+    k = K1 - 1
     if target is not None and target.dtype != draft.dtype:
         raise ValueError("target and draft logits must share a dtype")
+    dk = draft.shape[1]
+    if draft.shape[0] != B or draft.shape[2] != V or not (
+            dk == K1 or (dk == k and target is not None and not forks)):
+        raise ValueError(f"draft logits {tuple(draft.shape)} do not match [B, k+1, V] = "
+                         f"{(B, K1, V)} (or [B, k, V] without forks)")
+    if (not isinstance(draft_tokens, torch.Tensor) or draft_tokens.dtype != torch.int32
+            or not draft_tokens.is_contiguous() or tuple(draft_tokens.shape) != (B, k)):
+        raise ValueError(f"draft_tokens must be contiguous int32 {(B, k)}")
+    if (not isinstance(temperature, torch.Tensor) or temperature.dtype != torch.float32
+            or not temperature.is_contiguous() or tuple(temperature.shape) != (B,)):
+        raise ValueError(f"temperature must be contiguous float32 {(B,)}")
     b = SvBatch()
     b.B, b.k, b.V = int(B), int(k), int(V)
     b.dtype = _dtype_code(ref)
@@ -195,8 +225,16 @@ def _batch(target, draft, draft_tokens, temperature):
 
 
 def _f32(t, shape, name):
-    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape)):
         raise ValueError(f"{name} must be contiguous float32 {tuple(shape)}")
+    return t
+
+
+def _out(t, shape, dtype, name):
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"out[{name!r}] must be contiguous {dtype} {tuple(shape)}")
     return t
 
 
@@ -209,11 +247,30 @@ def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int
     int32, and optionally p_draft/q_draft [B,k] float32, fork_tokens
     [B,k+1,f] int32 / fork_probs [B,k+1,f] float32 and (f > 0, want_hits)
     cache_hit [B] int32."""
-    b = _batch(target, draft, draft_tokens, temperature)
+    if target is None:
+        raise ValueError("verify needs the target logits")
+    f = int(f)
+    if f < 0:
+        raise ValueError("f must be >= 0")
+    b = _batch(target, draft, draft_tokens, temperature, forks=f > 0)
     B, k = b.B, b.k
-    dev = target.device
+    if f > min(16, b.V - 1):
+        raise ValueError("f must be at most min(16, V - 1)")
     _f32(u_accept, (B, k), "u_accept")
     _f32(u_recover, (B, k + 1), "u_recover")
+    if out is not None:
+        _out(out.get("accept_len"), (B,), torch.int32, "accept_len")
+        _out(out.get("out_token"), (B,), torch.int32, "out_token")
+        for name in ("p_draft", "q_draft"):
+            if out.get(name) is not None:
+                _out(out[name], (B, k), torch.float32, name)
+        if f > 0:
+            _out(out.get("fork_tokens"), (B, k + 1, f), torch.int32, "fork_tokens")
+            _out(out.get("fork_probs"), (B, k + 1, f), torch.float32, "fork_probs")
+            if out.get("cache_hit") is not None:
+                _out(out["cache_hit"], (B,), torch.int32, "cache_hit")
+    dev = _same_device([target, draft, draft_tokens, temperature, u_accept, u_recover]
+                       + ([t for t in out.values() if t is not None] if out else []), "verify")
     if out is None:
         out = {
             "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
@@ -253,12 +310,16 @@ def residual_sample(target, draft, draft_tokens, temperature, position, u_recove
                     stream=None):
     """sv_residual_sample: returns dict with token [B] int32 and optionally
     residual [B,k+1,V] float32."""
+    if target is None:
+        raise ValueError("residual_sample needs the target logits")
     b = _batch(target, draft, draft_tokens, temperature)
     B, k, V = b.B, b.k, b.V
-    dev = target.device
-    if position.dtype != torch.int32 or not position.is_contiguous():
-        raise ValueError("position must be contiguous int32 [B]")
+    if (not isinstance(position, torch.Tensor) or position.dtype != torch.int32
+            or not position.is_contiguous() or tuple(position.shape) != (B,)):
+        raise ValueError(f"position must be contiguous int32 {(B,)}")
     _f32(u_recover, (B, k + 1), "u_recover")
+    dev = _same_device([target, draft, draft_tokens, temperature, position, u_recover],
+                       "residual_sample")
     out = {"token": torch.empty(B, dtype=torch.int32, device=dev)}
     res = None
     rs0 = rs1 = 0
@@ -281,9 +342,12 @@ def forked_topf(draft, draft_tokens, temperature, f: int,
                 workspace: Optional[Workspace] = None, stream=None):
     """sv_forked_topf: returns (tokens [B,k+1,f] int32, probs [B,k+1,f]
     float32)."""
-    b = _batch(None, draft, draft_tokens, temperature)
+    f = int(f)
+    b = _batch(None, draft, draft_tokens, temperature, forks=True)
     B, k = b.B, b.k
-    dev = draft.device
+    if not 1 <= f <= min(16, b.V - 1):
+        raise ValueError("f must be in [1, min(16, V - 1)]")
+    dev = _same_device([draft, draft_tokens, temperature], "forked_topf")
     toks = torch.empty(B, k + 1, f, dtype=torch.int32, device=dev)
     probs = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
     forks = SvForks(int(f), toks.data_ptr(), probs.data_ptr())
@@ -308,6 +372,7 @@ def cache_hit(fork_tokens, accept_len, out_token, stream=None):
     B, K1, f = fork_tokens.shape
     if tuple(accept_len.shape) != (B,) or tuple(out_token.shape) != (B,):
         raise ValueError("accept_len and out_token must be [B]")
+    _same_device([fork_tokens, accept_len, out_token], "cache_hit")
     hits = torch.empty(B, dtype=torch.int32, device=fork_tokens.device)
     code = lib().sv_cache_hit(int(B), int(K1 - 1), int(f), _ptr(fork_tokens), _ptr(accept_len),
                               _ptr(out_token), _ptr(hits), _stream_handle(stream))
@@ -323,11 +388,15 @@ def sample_temp(logits, temperature, uniforms, rows_per_temp: int = 1, stream=No
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be [rows, V] with V contiguous")
     rows, V = logits.shape
+    _dtype_code(logits)
+    if rows_per_temp < 1:
+        raise ValueError("rows_per_temp must be >= 1")
     if temperature.dtype != torch.float32 or not temperature.is_contiguous():
         raise ValueError("temperature must be contiguous float32")
-    if (temperature.numel() * rows_per_temp < rows):
+    if temperature.numel() * rows_per_temp < rows:
         raise ValueError("one temperature per rows_per_temp rows is needed")
     _f32(uniforms, (rows,), "uniforms")
+    _same_device([logits, temperature, uniforms], "sample_temp")
     toks = torch.empty(rows, dtype=torch.int32, device=logits.device)
     code = lib().sv_sample_temp(_ptr(logits), _dtype_code(logits), int(rows), int(V),
                                 logits.stride(0), _ptr(temperature), int(rows_per_temp),
@@ -343,9 +412,14 @@ def softmax_temp(logits, temperature, rows_per_temp: int = 1,
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be [rows, V] with V contiguous")
     rows, V = logits.shape
+    _dtype_code(logits)
+    if rows_per_temp < 1:
+        raise ValueError("rows_per_temp must be >= 1")
     if temperature.dtype != torch.float32 or not temperature.is_contiguous():
         raise ValueError("temperature must be contiguous float32")
-    dev = logits.device
+    if temperature.numel() * rows_per_temp < rows:
+        raise ValueError("one temperature per rows_per_temp rows is needed")
+    dev = _same_device([logits, temperature], "softmax_temp")
     Vp = (V + 3) // 4 * 4
     out = torch.empty(rows, Vp, dtype=torch.float32, device=dev)[:, :V]
     ws = workspace or default_workspace(dev, stream)
@@ -366,10 +440,17 @@ class PreparedVerify:
     def __init__(self, target, draft, draft_tokens, temperature, u_accept, u_recover,
                  f: int, out: dict, workspace: Workspace, stream=None):
         self._keep = (target, draft, draft_tokens, temperature, u_accept, u_recover, out)
-        self.batch = _batch(target, draft, draft_tokens, temperature)
+        self.batch = _batch(target, draft, draft_tokens, temperature, forks=f > 0)
         B, k = self.batch.B, self.batch.k
         _f32(u_accept, (B, k), "u_accept")
         _f32(u_recover, (B, k + 1), "u_recover")
+        _out(out.get("accept_len"), (B,), torch.int32, "accept_len")
+        _out(out.get("out_token"), (B,), torch.int32, "out_token")
+        if f > 0:
+            _out(out.get("fork_tokens"), (B, k + 1, f), torch.int32, "fork_tokens")
+            _out(out.get("fork_probs"), (B, k + 1, f), torch.float32, "fork_probs")
+        _same_device([target, draft, draft_tokens, temperature, u_accept, u_recover]
+                     + [t for t in out.values() if t is not None], "PreparedVerify")
         hits = out.get("cache_hit")
         self.forks = SvForks(int(f), out["fork_tokens"].data_ptr(),
                              out["fork_probs"].data_ptr(),
