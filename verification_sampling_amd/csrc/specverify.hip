@@ -38,320 +38,14 @@
 #include <algorithm>
 #include <atomic>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <type_traits>
 
 #include "specverify.h"
-#include "sv_device.h"
-#include "sv_stats.h"
+#include "sv_stream.h"
 
 namespace sv {
-
-constexpr double kLog2e = 1.4426950408889634074;
-
-enum Mode : int { kVerify = 0, kForks = 1, kResidual = 2, kSoftmax = 3 };
-
-// Largest vocabulary: k_decide keeps one pair of chunk totals per chunk of a
-// row in LDS (fp32 chunks hold 1024 elements).
-constexpr int kMaxChunks = 1024;
-constexpr int64_t kMaxV = (int64_t)kMaxChunks * kU * kLanes * 4;
-constexpr int kMaxSeg = 64;  // partials per row (one lane each when merged)
-constexpr int kDumpCap = 128;  // fork candidate vectors a k_stats wave passes on
-
-// Arrival counters sit 256 bytes apart: device-scope atomics to one memory
-// line are serialised.
-constexpr int64_t kCtrStride = 64;
-
-// Row record for k_write (residual distributions), written by k_decide.
-struct RowRec {
-  float tm;     // target reference
-  int targ;     // target argmax
-  double ts;    // target sum of 2^((x - tm) c)
-  float dm;     // draft reference (unmasked row)
-  int valid;
-  double ds;    // draft sum of 2^((y - dm) c)
-  double zr;    // total weight: sum of max(0, p - q), or of p at j = k
-};
-
-struct SeqRec {
-  int n;        // outcome position
-  int status;   // 0 error, 1 finished (greedy), 2 drawn at temperature > 0
-};
-
-struct Ws {
-  float* tm; double* ts; int* targ;     // [R * kMaxSeg] target segment partials
-  float* dm; double* ds; int* darg;     // [R * kMaxSeg] draft segment partials
-  float* dtv; int* dti;                 // [R * kMaxSeg * F] draft segment top-F
-  RowRec* rows;                         // [R]
-  SeqRec* seqs;                         // [B]
-  float* xd; float* yd;                 // [R] the drafted token's logits, seen by k_stats
-  int* cn; int* cpos;                   // [R * kMaxSeg], [R * kMaxSeg * kDumpCap] fork candidates
-  double* ctr;                          // [tasks * cpr] k_decide chunk totals
-  unsigned* cnt;                        // [tasks * kCtrStride] k_decide arrivals
-};
-
-struct Params {
-  const void* T; int64_t t_seq, t_row;
-  const void* D; int64_t d_seq, d_row;
-  const int32_t* drafts;
-  const float* tau;
-  const float* u_acc;
-  const float* u_rec;
-  const int32_t* position;
-  int32_t B, k, V, f, F, mode, rows_all, want_q;
-  int32_t cpr;             // chunks per row
-  int32_t nslab;           // slabs per row
-  int32_t nparts;          // k_stats segments (partials) per row
-  int32_t nbs;             // k_decide blocks per task row
-  int32_t fsplit;          // k_decide fork blocks per sequence
-  int64_t nslots;          // row slots of k_stats
-  int64_t rows_per_temp;   // softmax
-  int32_t* accept_len;
-  int32_t* out_token;
-  float* p_draft;
-  float* q_draft;
-  int32_t* fork_tok;
-  float* fork_prob;
-  float* out; int64_t out_seq, out_row;
-  Ws ws;
-};
-
-__device__ __forceinline__ bool tau_ok(float t) { return t >= 0.0f && t < pos_inf(); }
-
-__device__ __forceinline__ float slot_tau(const Params& P, int64_t slot, int b) {
-  if (P.mode == kSoftmax) return P.tau[slot / P.rows_per_temp];
-  return P.tau[b];
-}
-
-// Row slot -> (sequence, position) of k_stats.
-__device__ __forceinline__ void slot_to_bj(const Params& P, int64_t slot, int& b, int& j) {
-  if (P.mode == kSoftmax) { b = (int)slot; j = 0; return; }
-  if (P.mode == kResidual && !P.rows_all) { b = (int)slot; j = P.position[b]; return; }
-  b = (int)(slot / (P.k + 1));
-  j = (int)(slot - (int64_t)b * (P.k + 1));
-}
-
-// Slot of row (b, j) in the partial arrays.
-__device__ __forceinline__ int64_t slot_of(const Params& P, int b, int j) {
-  if (P.mode == kResidual && !P.rows_all) return b;
-  return (int64_t)b * (P.k + 1) + j;
-}
-
-template <typename In>
-__device__ __forceinline__ const In* trow_ptr(const Params& P, int b, int j) {
-  return reinterpret_cast<const In*>(P.T) + (int64_t)b * P.t_seq + (int64_t)j * P.t_row;
-}
-template <typename In>
-__device__ __forceinline__ const In* drow_ptr(const Params& P, int b, int j) {
-  return reinterpret_cast<const In*>(P.D) + (int64_t)b * P.d_seq + (int64_t)j * P.d_row;
-}
-template <typename In>
-__device__ __forceinline__ float load_logit(const In* row, int64_t t) {
-  if constexpr (sizeof(In) == 4) return row[t];
-  else return __uint_as_float(((uint32_t)row[t]) << 16);
-}
-
-__device__ __forceinline__ float scale_of(float tau) {
-  return (float)(kLog2e / (double)tau);
-}
-
-// Which tensors / statistics a row needs.
-struct RowPlan {
-  bool pos_ok, readT, readD, topf, greedy, tok;
-  int mask_id;  // element left out of the draft's masked statistics (-1: none)
-  int d_id;     // the drafted token of the row (-1: none)
-  int nf;       // forks asked for (f <= F)
-};
-
-__device__ __forceinline__ RowPlan plan_row(const Params& P, int b, int j, float tau) {
-  RowPlan r;
-  r.tok = tau_ok(tau);
-  r.greedy = (tau == 0.0f) || !r.tok;
-  r.pos_ok = (j >= 0 && j <= P.k);
-  const bool forks = (P.mode == kForks) || (P.mode == kVerify && P.f > 0);
-  r.topf = forks && r.pos_ok;
-  r.readT = r.pos_ok && P.mode != kForks;
-  if (P.mode == kForks) r.readD = r.pos_ok;
-  else if (P.mode == kVerify)
-    r.readD = r.pos_ok && (j < P.k ? (tau != 0.0f || P.want_q || P.f > 0) : (P.f > 0));
-  else if (P.mode == kResidual) r.readD = r.pos_ok && j < P.k;
-  else r.readD = false;
-  r.mask_id = -1;
-  r.d_id = -1;
-  r.nf = P.f;
-  if (r.pos_ok && j < P.k && P.mode != kSoftmax) {
-    const int d = P.drafts[(int64_t)b * P.k + j];
-    r.d_id = d;  // out-of-range ids match no element
-    if (r.topf) r.mask_id = d;
-  }
-  return r;
-}
-
-// ================================================================ k_stats
-
-// The drafted token leaves the draft row's masked statistics: the element
-// is set to -inf in the lane that holds it (one chunk per row).
-template <typename In>
-struct Vec4 {
-  uint4 v[kU];
-};
-
-template <typename In>
-__device__ __noinline__ Vec4<In> mask_token(uint4 v0, uint4 v1, uint4 v2, uint4 v3, int e_base,
-                                            int mask_id) {
-  constexpr int VEC = Elem<In>::VEC;
-  static_assert(kU == 4, "mask_token takes four vectors");
-  Vec4<In> r;
-  r.v[0] = v0; r.v[1] = v1; r.v[2] = v2; r.v[3] = v3;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if (e_base + u * slab_elems<In>() + e == mask_id) set_neg_inf<In>(r.v[u], e);
-    }
-  }
-  return r;
-}
-
-// The value of element `id` if this lane holds it in the chunk (else -inf),
-// and whether it does.
-template <typename In>
-__device__ __noinline__ float2 pick_elem(uint4 v0, uint4 v1, uint4 v2, uint4 v3, int e_base,
-                                         int id) {
-  constexpr int VEC = Elem<In>::VEC;
-  static_assert(kU == 4, "pick_elem takes four vectors");
-  const uint4 raw[kU] = {v0, v1, v2, v3};
-  float x = neg_inf(), found = 0.0f;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if (e_base + u * slab_elems<In>() + e == id) { x = elem<In>(raw[u], e); found = 1.0f; }
-    }
-  }
-  return make_float2(x, found);
-}
-
-struct WaveState {
-  Warm tw, dw;    // temperature > 0
-  Greedy tg, dg;  // temperature 0
-  int nc;         // fork candidate slots in use (this lane)
-  float kv;       // fork candidate threshold (wave-uniform)
-};
-
-// Writes element id of a chunk (held by one lane, if any) to *out.
-template <typename In>
-__device__ __forceinline__ void capture(const uint4 (&raw)[kU], int e_base, int id, float* out) {
-  const float2 r = pick_elem<In>(raw[0], raw[1], raw[2], raw[3], e_base, id);
-  if (r.y != 0.0f) *out = r.x;
-}
-
-// One chunk of a segment, already in registers.  RT / RD: the target / draft
-// row is read; GREEDY: temperature 0; FIRST: the segment's first chunk.
-// cs: the chunk's first element (wave-uniform); e_base = cs + lane * VEC;
-// nv: vectors of the chunk inside the segment (the others read as -inf).
-// The drafted token's logits are written to xd / yd when the chunk holds it.
-template <typename In, int F, bool RT, bool RD, bool GREEDY, bool FIRST>
-__device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* drow,
-                                            const uint4 (&traw)[kU], uint4 (&draw)[kU],
-                                            int cs, int e_base, int nv, float c, WaveState& st,
-                                            CandLds<F>* L, float* xd, float* yd) {
-  constexpr int SLAB = slab_elems<In>();
-  constexpr int CH = chunk_elems<In>();
-  // only vectors [0, nv) of the chunk belong to this segment
-  const bool has_d = pl.d_id >= cs && pl.d_id < cs + nv * SLAB;
-  if constexpr (RT) {
-    if (has_d) capture<In>(traw, e_base, pl.d_id, xd);
-    float m8[kU];
-    if constexpr (GREEDY) greedy_fold<In>(st.tg, traw, e_base, true, m8);
-    else warm_fold<In, FIRST>(st.tw, traw, c, m8);
-  }
-  if constexpr (RD) {
-    if (has_d) capture<In>(draw, e_base, pl.d_id, yd);
-    if (pl.mask_id >= cs && pl.mask_id < cs + CH) {
-      const Vec4<In> m = mask_token<In>(draw[0], draw[1], draw[2], draw[3], e_base, pl.mask_id);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) draw[u] = m.v[u];
-    }
-    float m8[kU], vs[kU];
-    if constexpr (GREEDY) greedy_fold<In>(st.dg, draw, e_base, !pl.topf, m8);
-    else warm_fold_vs<In, FIRST>(st.dw, draw, c, m8, vs);
-    if constexpr (F > 0) {
-      if (pl.topf) {
-        unsigned bits = 0;
-        if constexpr (FIRST) {
-          // at least f vectors reach the f-th largest lane maximum, so every
-          // element of the segment's top-f does; the first chunk's
-          // candidates are the vectors there
-          float lm = m8[0];
-#pragma unroll
-          for (int u = 1; u < kU; ++u) lm = fmaxf(lm, m8[u]);
-          st.kv = wave_fth_largest<F>(lm, pl.nf);
-#pragma unroll
-          for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
-        } else if (!(st.kv > neg_inf())) {
-          bits = (1u << kU) - 1u;  // fewer than F elements seen: all are candidates
-        } else if constexpr (GREEDY) {
-#pragma unroll
-          for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
-        } else {
-          // an element at or above kv has a term 2^(x c - hi) of at least
-          // 2^(kv c - hi); a vector whose sum of terms is below that (less a
-          // margin for rounding) holds no such element
-          const float eth = __builtin_amdgcn_exp2f(fmaf(st.kv, c, -st.dw.hi)) * 0.999999f;
-#pragma unroll
-          for (int u = 0; u < kU; ++u) bits |= (vs[u] >= eth) ? (1u << u) : 0u;
-        }
-        bits &= (1u << nv) - 1u;  // vectors past the segment belong to the next one
-        if (__ballot(bits != 0u)) {
-          cand_append<F>(L, bits, e_base, SLAB, st.nc);
-          if (__ballot(st.nc > kCandSlots - kU))
-            cand_reduce<In, F, 2>(L, drow, V, pl.mask_id, st.nc, st.kv);
-        }
-      }
-    }
-  }
-}
-
-// A segment of slabs [s0, s1) of one row, a chunk (kU slabs) at a time; the
-// next chunk's loads are issued before the current chunk is folded.
-template <typename In, int F, bool RT, bool RD, bool GREEDY>
-__device__ __forceinline__ void stats_segment(const RowPlan& pl, int V, const In* trow,
-                                              const In* drow, int s0, int s1, float c,
-                                              WaveState& st, CandLds<F>* L, float* xd,
-                                              float* yd) {
-  constexpr int SLAB = slab_elems<In>();
-  constexpr int VEC = Elem<In>::VEC;
-  const int lane = lane_id();
-  const int nch = (s1 - s0 + kU - 1) / kU;
-  const int slim = min(s1, V / SLAB);  // slabs [.., slim) lie inside the row
-  uint4 ta[kU], da[kU], tb[kU], db[kU];
-  auto load = [&](uint4 (&t)[kU], uint4 (&d)[kU], int i) {
-    const int sl = s0 + i * kU;
-    const int nv = min(kU, s1 - sl);
-    const bool full = sl + kU <= slim;
-    const int eb = sl * SLAB + lane * VEC;
-    if constexpr (RT) load_chunk<In>(trow, eb, nv, V, full, t);
-    if constexpr (RD) load_chunk<In>(drow, eb, nv, V, full, d);
-  };
-  auto fold = [&](const uint4 (&t)[kU], uint4 (&d)[kU], int i, auto first) {
-    const int sl = s0 + i * kU;
-    const int nv = min(kU, s1 - sl);
-    stats_chunk<In, F, RT, RD, GREEDY, decltype(first)::value>(pl, V, drow, t, d, sl * SLAB,
-                                                               sl * SLAB + lane * VEC, nv, c,
-                                                               st, L, xd, yd);
-  };
-  load(ta, da, 0);
-  if (nch > 1) load(tb, db, 1);
-  fold(ta, da, 0, std::true_type{});
-  for (int i = 1; i < nch; i += 2) {
-    if (i + 1 < nch) load(ta, da, i + 1);
-    fold(tb, db, i, std::false_type{});
-    if (i + 1 >= nch) break;
-    if (i + 2 < nch) load(tb, db, i + 2);
-    fold(ta, da, i + 1, std::false_type{});
-  }
-}
 
 // Four resident waves per SIMD: the register budget (128) the folding code
 // needs, and enough bytes in flight with the one-chunk prefetch.
@@ -359,9 +53,8 @@ __device__ __forceinline__ void stats_segment(const RowPlan& pl, int V, const In
 #define SV_STATS_WAVES_PER_EU 4
 #endif
 
-// One wave per (row slot, segment): segment g of a row covers slabs
-// [g * nslab / nseg, (g + 1) * nslab / nseg).  The grid is one resident
-// round of waves.
+// One wave per (row slot, segment).  The grid is one resident round of
+// waves.
 template <typename In, int F>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params P) {
@@ -372,150 +65,35 @@ __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params 
   const int seg = (int)(task - slot * P.nparts);
   int b, j;
   slot_to_bj(P, slot, b, j);
-  b = uniform(b);
-  j = uniform(j);
-  const float tau = uniform(slot_tau(P, slot, b));
-  const RowPlan pl = plan_row(P, b, j, tau);
-  const float c = pl.greedy ? 0.0f : scale_of(tau);
-  const int lane = lane_id();
-  const Ws& W = P.ws;
-  const int s0 = (int)((int64_t)seg * P.nslab / P.nparts);
-  const int s1 = (int)((int64_t)(seg + 1) * P.nslab / P.nparts);
-  const In* trow = pl.readT ? trow_ptr<In>(P, b, j) : nullptr;
-  const In* drow = pl.readD ? drow_ptr<In>(P, b, j) : nullptr;
-
-  CandLds<F>* L = &s_cand[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
-  WaveState st;
-  warm_init(st.tw); warm_init(st.dw);
-  greedy_init(st.tg); greedy_init(st.dg);
-  st.nc = 0;
-  st.kv = neg_inf();
-  if constexpr (F > 0) {
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < F; ++r) { L->wv[r] = neg_inf(); L->wi[r] = kEmptyId; }
-    }
-  }
-  float* xd = W.xd + slot;
-  float* yd = W.yd + slot;
-  if (s1 > s0) {
-    const int V = P.V;
-    if (pl.readT && pl.readD) {
-      if (pl.greedy) stats_segment<In, F, true, true, true>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
-      else stats_segment<In, F, true, true, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
-    } else if (pl.readT) {
-      if (pl.greedy) stats_segment<In, F, true, false, true>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
-      else stats_segment<In, F, true, false, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
-    } else if (pl.readD) {
-      if (pl.greedy) stats_segment<In, F, false, true, true>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
-      else stats_segment<In, F, false, true, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
-    }
-  }
-  const int64_t part = slot * kMaxSeg + seg;
-  if constexpr (F > 0) {
-    if (pl.topf && pl.readD) {
-      // pass the candidate positions on, compacted; rank them here only if
-      // they do not fit
-      int incl = wave_inclusive_scan_i(st.nc);
-      int total = readlane_i(incl, kLanes - 1);
-      if (total > kDumpCap) {
-        cand_reduce<In, F, 8>(L, drow, P.V, pl.mask_id, st.nc, st.kv);
-        incl = 0;
-        total = 0;
-      }
-      int* dst = W.cpos + part * kDumpCap + (incl - st.nc);
-      for (int i = 0; i < st.nc; ++i) dst[i] = L->pos[i][lane];
-      if (lane == 0) W.cn[part] = total;
-    }
-  }
-
-  if (pl.readT) {
-    const WaveStats ws = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
-    if (lane == 0) { W.tm[part] = ws.m; W.ts[part] = ws.s; W.targ[part] = ws.arg; }
-  }
-  if (pl.readD) {
-    const WaveStats ws = pl.greedy ? wave_finish_greedy(st.dg) : wave_finish_warm(st.dw, c);
-    if (lane == 0) { W.dm[part] = ws.m; W.ds[part] = ws.s; W.darg[part] = ws.arg; }
-    if constexpr (F > 0) {
-      if (pl.topf && lane < F) {
-        W.dtv[part * F + lane] = L->wv[lane];
-        W.dti[part * F + lane] = L->wi[lane];
-      }
-    }
-  }
-}
-
-// ================================================================ merging
-
-struct Merged {
-  float m; double s; int arg;
-};
-
-// Row reference / sum / argmax from the segment partials of one slot; every
-// lane gets the result.  (k_write; k_decide merges from registers.)
-__device__ __forceinline__ Merged merge_partials(const float* pm, const double* ps,
-                                                 const int* parg, int64_t base, int np,
-                                                 bool greedy, double cd) {
-  const int lane = lane_id();
-  float mi = neg_inf();
-  double si = 0.0;
-  int ai = kEmptyId;
-  if (lane < np) { mi = pm[base + lane]; si = ps[base + lane]; ai = parg[base + lane]; }
-  const float M = wave_max(mi);
-  double s = 0.0;
-  int arg = kEmptyId;
-  if (greedy) {
-    if (lane < np && mi == M) arg = ai;
-  } else if (finitef(M) && mi > neg_inf()) {
-    s = si * exp2(((double)mi - (double)M) * cd);
-  }
-  Merged r;
-  r.m = M;
-  r.s = wave_sum(s);
-  r.arg = wave_min(arg);
-  return r;
-}
-
-// The same from values already in the lanes (lane i holds partial i, empty
-// lanes hold -inf).
-__device__ __forceinline__ Merged merge_lanes(float mi, double si, int ai, bool greedy, double cd) {
-  const float M = wave_max(mi);
-  double s = 0.0;
-  int arg = kEmptyId;
-  if (greedy) {
-    if (mi == M) arg = ai;
-  } else if (finitef(M) && mi > neg_inf()) {
-    s = si * exp2(((double)mi - (double)M) * cd);
-  }
-  Merged r;
-  r.m = M;
-  r.s = wave_sum(s);
-  r.arg = wave_min(arg);
-  return r;
+  stream_segment<In, F>(P, slot, uniform(b), uniform(j), seg, P.nparts,
+                        &s_cand[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)]);
 }
 
 // The candidate vectors the segments of row (b, j) passed on (cnt: this
-// lane's segment's count, lanes < np): positions, then vectors, are loaded
-// a round of 64 * kRound at a time; their elements (id < V, id != mask_id)
-// at or above the f-th largest of the lanes' maxima over the loaded
-// vectors go into this lane's list.  That bound never drops one of the
-// row's top-f: at least f of the loaded elements reach it.  With nhalf = 2,
-// two waves share the row: wave `half` takes every other round.
+// lane's segment's count, lanes < np), a round of 64 * kRound at a time:
+// their positions and maxima are loaded first, and the f-th largest of
+// those maxima (f distinct elements reach it, so it is a lower bound of the
+// row's f-th best) raises the threshold kv.  Only the vectors whose maximum
+// reaches kv, or is unknown (tagged inexact), are re-read; their elements
+// (id < V, id != mask_id) at or above kv go into this lane's list.  With
+// nhalf = 2, two waves share the row: wave `half` takes every other round.
 template <typename In, int F>
 __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, int64_t base,
                                                 int np, int cnt, int mask_id, int half,
                                                 int nhalf, TopList<F>& mine) {
   if constexpr (F > 0) {
     constexpr int VEC = Elem<In>::VEC;
-    constexpr int kRound = 2;
+    constexpr int kRound = 4;
     const int lane = lane_id();
     const int mycnt = lane < np ? cnt : 0;
     const int incl = wave_inclusive_scan_i(mycnt);
     const int total = readlane_i(incl, kLanes - 1);
     const In* drow = drow_ptr<In>(P, b, j);
     const int V = P.V;
+    float kv = neg_inf();
     for (int t0 = half * kLanes * kRound; t0 < total; t0 += nhalf * kLanes * kRound) {
       int pos[kRound];
+      float vm[kRound];
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
         const int t = t0 + q * kLanes + lane;
@@ -542,39 +120,32 @@ __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, i
         const int seg = min(lo, np - 1);
         const int before = __shfl(incl, seg) - __shfl(mycnt, seg);
         pos[q] = -1;
-        if (t < total) pos[q] = P.ws.cpos[(base + seg) * kDumpCap + (t - before)];
-      }
-      uint4 v[kRound];
-#pragma unroll
-      for (int q = 0; q < kRound; ++q) {
-        v[q] = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
-                          Elem<In>::kNegInfWord);
-        if (pos[q] >= 0) load_vec<In>(drow, pos[q], V, v[q]);
-      }
-      float lm = neg_inf();
-      bool any = false;
-#pragma unroll
-      for (int q = 0; q < kRound; ++q) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int id = pos[q] + e;
-          if (pos[q] >= 0 && id < V && id != mask_id) { lm = fmaxf(lm, elem<In>(v[q], e)); any = true; }
+        vm[q] = neg_inf();
+        if (t < total) {
+          const int64_t e = (base + seg) * kDumpCap + (t - before);
+          pos[q] = P.ws.cpos[e];
+          vm[q] = P.ws.cvm[e];
         }
       }
-      // a lane with an element at -inf still counts towards the F
-      const float key = any ? lm : neg_inf();
-      const unsigned long long have = __ballot(any);
-      const float kvr = (__popcll(have) >= P.f) ? wave_fth_largest<F>(key, P.f) : neg_inf();
+      // inexact candidates hold -inf: they add nothing to the bound
+      kv = fmaxf(kv, fth_largest_multi<kRound>(vm, P.f));
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
-        float thr = fmaxf(kvr, mine.v[F - 1]);
+        const bool inexact = pos[q] >= 0 && (pos[q] & kCandInexact);
+        const int p0 = pos[q] >= 0 ? (pos[q] & ~kCandInexact) : -1;
+        const bool keep = p0 >= 0 && (inexact || vm[q] >= kv);
+        if (!__ballot(keep)) continue;
+        uint4 v = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
+                             Elem<In>::kNegInfWord);
+        if (keep) load_vec<In>(drow, p0, V, v);
+        float thr = fmaxf(kv, mine.v[F - 1]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float x = elem<In>(v[q], e);
-          const int id = pos[q] + e;
-          if (pos[q] >= 0 && id < V && id != mask_id && x >= thr) {
+          const float x = elem<In>(v, e);
+          const int id = p0 + e;
+          if (keep && id < V && id != mask_id && x >= thr) {
             mine.insert(x, id);
-            thr = fmaxf(kvr, mine.v[F - 1]);
+            thr = fmaxf(kv, mine.v[F - 1]);
           }
         }
       }
@@ -752,85 +323,10 @@ __device__ __forceinline__ void row_stat(const Params& P, int b, int j, float ta
   }
 }
 
-// ================================================================ residual
-
-// Per-element residual weight r = max(0, p - q) and target probability p
-// from the merged row statistics (fp32 terms; references split exactly as
-// in the statistics pass).
-struct ResidCoef {
-  float c, thi, tscale, dhi, dscale;
-  bool has_q;
-};
-
-__device__ __forceinline__ ResidCoef resid_coef(float tm, double ts, float dm, double ds,
-                                                float c, bool has_q) {
-  ResidCoef k;
-  k.c = c;
-  k.thi = tm * c;
-  const float tlo = fmaf(tm, c, -k.thi);
-  k.tscale = (float)(exp2(-(double)tlo) / ts);
-  k.has_q = has_q;
-  k.dhi = 0.0f;
-  k.dscale = 0.0f;
-  if (has_q) {
-    k.dhi = dm * c;
-    const float dlo = fmaf(dm, c, -k.dhi);
-    k.dscale = (float)(exp2(-(double)dlo) / ds);
-  }
-  return k;
-}
-
-__device__ __forceinline__ void resid_elem(const ResidCoef& k, float x, float y, float& p,
-                                           float& r) {
-  p = __builtin_amdgcn_exp2f(fmaf(x, k.c, -k.thi)) * k.tscale;
-  if (k.has_q) {
-    const float q = __builtin_amdgcn_exp2f(fmaf(y, k.c, -k.dhi)) * k.dscale;
-    r = fmaxf(p - q, 0.0f);
-  } else {
-    r = p;
-  }
-}
-
-// Pairwise fp32 sum of one vector's weights (fixed order).
-template <int N>
-__device__ __forceinline__ float vec_sum(const float (&w)[N]) {
-  float a[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) a[e] = w[e];
-#pragma unroll
-  for (int h = N / 2; h > 0; h >>= 1) {
-#pragma unroll
-    for (int e = 0; e < h; ++e) a[e] = a[e] + a[e + h];
-  }
-  return a[0];
-}
-
-// The weights of a lane's chunk summed: per vector the fp32 sum of r (which
-// is p where there is no q), the vectors added in fp64.
-template <typename In>
-__device__ __forceinline__ double chunk_rsum(const ResidCoef& kc, const uint4 (&t)[kU],
-                                             const uint4 (&d)[kU]) {
-  constexpr int VEC = Elem<In>::VEC;
-  double acc = 0.0;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    float r[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float p;
-      resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p, r[e]);
-    }
-    acc += (double)vec_sum<VEC>(r);
-  }
-  return acc;
-}
-
 // ================================================================ k_decide
 
 constexpr int kDecideWaves = 16;
 constexpr int kDecideBlock = kDecideWaves * kLanes;
-
-constexpr int kTotRegs = 4;  // chunk totals the drawing wave keeps in registers (x 64)
 
 struct DecideLds {
   RowStat rs[kMaxK + 1];
@@ -840,29 +336,6 @@ struct DecideLds {
   int wi[kDecideWaves][kMaxF];
   int n, status;
 };
-
-// Overwrites the per-sequence outputs of an error sequence.
-__device__ __forceinline__ void write_seq_error(const Params& P, int b) {
-  const int lane = lane_id();
-  const float nan = __uint_as_float(0x7fc00000u);
-  const int K1 = P.k + 1;
-  if (P.fork_tok) {
-    for (int t = lane; t < K1 * P.f; t += kLanes) {
-      P.fork_tok[(int64_t)b * K1 * P.f + t] = -1;
-      if (P.fork_prob) P.fork_prob[(int64_t)b * K1 * P.f + t] = nan;
-    }
-  }
-  if (P.mode == kVerify) {
-    for (int t = lane; t < P.k; t += kLanes) {
-      if (P.p_draft) P.p_draft[(int64_t)b * P.k + t] = nan;
-      if (P.q_draft) P.q_draft[(int64_t)b * P.k + t] = nan;
-    }
-  }
-  if (lane == 0) {
-    if (P.accept_len) P.accept_len[b] = -1;
-    if (P.out_token) P.out_token[b] = -1;
-  }
-}
 
 // Wave 0 of a k_decide block: validity, acceptance tests, first rejection
 // (ballot over positions) and, when write_outputs, the per-sequence outputs.
@@ -948,10 +421,10 @@ __device__ __forceinline__ void decide_sequence(const Params& P, int b, const De
     const unsigned long long rej = __ballot(lane < k && !acc);
     const int n = rej ? (__ffsll((long long)rej) - 1) : k;
     n_out = n;
-    if (write_outputs && lane == 0) P.accept_len[b] = n;
+    if (write_outputs && lane == 0) st_dev(P.accept_len + b, n);
     if (greedy) {
       status = 1;
-      if (write_outputs && lane == 0) P.out_token[b] = S.rs[n].targ;
+      if (write_outputs && lane == 0) st_dev(P.out_token + b, S.rs[n].targ);
     } else {
       status = 2;
     }
@@ -959,7 +432,7 @@ __device__ __forceinline__ void decide_sequence(const Params& P, int b, const De
     n_out = pos;
     if (greedy) {
       status = 1;
-      if (write_outputs && lane == 0) P.out_token[b] = S.rs[pos].targ;
+      if (write_outputs && lane == 0) st_dev(P.out_token + b, S.rs[pos].targ);
     } else {
       status = 2;
     }
@@ -968,122 +441,32 @@ __device__ __forceinline__ void decide_sequence(const Params& P, int b, const De
   }
 }
 
-// The draw by one wave: the chunk from the per-chunk totals (device-scope
-// loads), then the vector (slab by slab, lanes inside), then the element;
-// each time the first whose running total passes u*Z among positive
-// weights, or the last positive one if rounding leaves none.
-template <typename In>
-__device__ __forceinline__ int resid_draw(const Params& P, const double* tot,
-                                          const double (&tc)[kTotRegs], const In* trow,
-                                          const In* drow, const ResidCoef& kc, double Z,
-                                          double u) {
-  constexpr int VEC = Elem<In>::VEC;
-  constexpr int64_t SLAB = slab_elems<In>();
+// Speculation-cache lookup of sequence b, once its outcome and its forks
+// are written (device-scope loads: they may come from other blocks): the
+// index of the outcome token among the forks of the outcome position, else
+// -1.  One wave.
+__device__ __forceinline__ void write_hit(const Params& P, int b) {
   const int lane = lane_id();
-  const int cpr = P.cpr;
-  const double target = u * Z;
+  const int K1 = P.k + 1;
+  const int n = uniform(ld_dev(P.accept_len + b));
+  const int t = uniform(ld_dev(P.out_token + b));
+  int hit = -1;
+  if (n >= 0 && n <= P.k && t >= 0) {
+    int tok = -1;
+    if (lane < P.f) tok = ld_dev(P.fork_tok + ((int64_t)b * K1 + n) * P.f + lane);
+    const unsigned long long m = __ballot(lane < P.f && tok == t);
+    hit = m ? (__ffsll((long long)m) - 1) : -1;
+  }
+  if (lane == 0) P.hits[b] = hit;
+}
 
-  // 1. chunk
-  int cstar = -1, clast = -1;
-  double before = 0.0, before_last = 0.0, carry = 0.0;
-  for (int g = 0; g < cpr; g += kLanes) {
-    const int ch = g + lane;
-    double w = 0.0;
-    if (cpr <= kTotRegs * kLanes) {
-#pragma unroll
-      for (int q = 0; q < kTotRegs; ++q)
-        if (q * kLanes == g) w = tc[q];
-    } else if (ch < cpr) {
-      w = ld_dev(tot + ch);
-    }
-    const double incl = carry + wave_inclusive_scan(w);
-    double excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = carry;
-    const unsigned long long hit = __ballot(ch < cpr && w > 0.0 && incl > target);
-    if (cstar < 0 && hit) {
-      const int l = __ffsll((long long)hit) - 1;
-      cstar = g + l;
-      before = readlane_d(excl, l);
-    }
-    const unsigned long long posm = __ballot(ch < cpr && w > 0.0);
-    if (posm) {
-      const int l = 63 - __clzll((long long)posm);
-      clast = g + l;
-      before_last = readlane_d(excl, l);
-    }
-    carry = readlane_d(incl, kLanes - 1);
-  }
-  if (cstar < 0) { cstar = clast; before = before_last; }
-  if (cstar < 0) { cstar = 0; before = 0.0; }
-
-  // 2. re-read that chunk; vector sums scanned slab by slab
-  const int64_t sl = (int64_t)cstar * kU;
-  const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
-  const int eb = (int)(sl * SLAB) + lane * VEC;
-  uint4 t[kU], d[kU];
-  load_chunk<In>(trow, eb, nv, P.V, false, t);
-  if (kc.has_q) {
-    load_chunk<In>(drow, eb, nv, P.V, false, d);
-  } else {
-#pragma unroll
-    for (int u = 0; u < kU; ++u) d[u] = make_uint4(0, 0, 0, 0);
-  }
-  float w[kU][VEC];
-  float vsum[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    float r[VEC], p[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      resid_elem(kc, elem<In>(t[u], e), kc.has_q ? elem<In>(d[u], e) : 0.0f, p[e], r[e]);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) w[u][e] = r[e];
-    vsum[u] = vec_sum<VEC>(r);
-  }
-  int ustar = -1, lstar = 0, ulast = -1, llast = 0;
-  double my_ex[kU];  // this lane's running total before its vector, per slab
-  carry = before;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const double incl = carry + wave_inclusive_scan((double)vsum[u]);
-    double excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = carry;
-    my_ex[u] = excl;
-    const unsigned long long hit = __ballot(vsum[u] > 0.0f && incl > target);
-    if (ustar < 0 && hit) {
-      ustar = u;
-      lstar = __ffsll((long long)hit) - 1;
-    }
-    const unsigned long long posm = __ballot(vsum[u] > 0.0f);
-    if (posm) {
-      ulast = u;
-      llast = 63 - __clzll((long long)posm);
-    }
-    carry = readlane_d(incl, kLanes - 1);
-  }
-  if (ustar < 0) { ustar = ulast; lstar = llast; }
-  if (ustar < 0) { ustar = 0; lstar = 0; }
-
-  // 3. the element inside lane lstar's vector ustar
-  int tokv = -1;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    if (u == ustar) {
-      int tk = -1, vlast = -1;
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        acc += w[u][e];
-        if (w[u][e] > 0.0f) {
-          const int id = (int)(eb + (int64_t)u * SLAB + e);
-          vlast = id;
-          if (tk < 0 && my_ex[u] + (double)acc > target) tk = id;
-        }
-      }
-      tokv = tk < 0 ? vlast : tk;
-    }
-  }
-  return readlane_i(tokv, lstar);
+// One of the lookup's two inputs of sequence b (the drawn token, or the
+// forks ranked beside the draw) has been written by the calling block, all
+// of whose waves have waited for their stores; the second arrival writes
+// the lookup.  One wave.
+__device__ __forceinline__ void hit_input_ready(const Params& P, int b) {
+  if (!P.hits) return;
+  if (arrive_last(seq_ctr(P.ws, b, kCtrHits), 2u)) write_hit(P, b);
 }
 
 // P.nbs blocks per task row: a task row is a sequence (verify, forks,
@@ -1151,11 +534,18 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
                                    ? 0.0f
                                    : (float)(exp2(((double)v - (double)qm) * cd) / qs);
             const int64_t o = ((int64_t)b * K1 + j) * P.f + r;
-            P.fork_tok[o] = top.i[r];
+            st_dev(P.fork_tok + o, top.i[r]);
             if (P.fork_prob) P.fork_prob[o] = prob;
           }
         }
       }
+    }
+    if (P.hits) {
+      // the sequence's last fork block to finish hands its forks to the lookup
+      vm_complete();
+      __syncthreads();
+      if (w == 0 && arrive_last(seq_ctr(P.ws, b, kCtrForks), (unsigned)P.fsplit))
+        hit_input_ready(P, b);
     }
     return;
   }
@@ -1204,7 +594,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
                                      ? 0.0f
                                      : (float)(exp2(((double)v - (double)qm) * cd) / qs);
               const int64_t o = ((int64_t)b * K1 + j) * P.f + r;
-              P.fork_tok[o] = top.i[r];
+              st_dev(P.fork_tok + o, top.i[r]);
               if (P.fork_prob) P.fork_prob[o] = prob;
             }
           }
@@ -1213,9 +603,14 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
       }
       if (lane < P.f) {
         const int64_t o = ((int64_t)b * K1 + j) * P.f + lane;
-        P.fork_tok[o] = S.rs[j].ftok[lane];
+        st_dev(P.fork_tok + o, S.rs[j].ftok[lane]);
         if (P.fork_prob) P.fork_prob[o] = S.rs[j].fprob[lane];
       }
+    }
+    if (P.hits) {
+      vm_complete();
+      __syncthreads();
+      if (w == 0) hit_input_ready(P, b);
     }
     return;
   }
@@ -1264,10 +659,17 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
     for (int j = w; j < K1; j += kDecideWaves) {
       if (lane < P.f) {
         const int64_t o = ((int64_t)b * K1 + j) * P.f + lane;
-        P.fork_tok[o] = S.rs[j].ftok[lane];
+        st_dev(P.fork_tok + o, S.rs[j].ftok[lane]);
         if (P.fork_prob) P.fork_prob[o] = S.rs[j].fprob[lane];
       }
     }
+  }
+  if (owner && P.hits && status != 2) {
+    // greedy or error: the owner wrote the token and the forks (-1 for an
+    // error sequence) itself
+    vm_complete();
+    __syncthreads();
+    if (w == 0) write_hit(P, b);
   }
   if (status != 2 || P.mode == kForks) return;
 
@@ -1324,7 +726,9 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   vm_complete();
   __syncthreads();
   if (w != 0) return;
-  if (!arrive_last(P.ws.cnt + task * kCtrStride, (unsigned)P.nbs)) return;
+  unsigned* ctr_arrive = (P.mode == kResidual && P.rows_all) ? row_ctr(P.ws, task)
+                                                              : seq_ctr(P.ws, task, kCtrDraw);
+  if (!arrive_last(ctr_arrive, (unsigned)P.nbs)) return;
 
   // 5. the last block: totals (chunk order) and the draw
   double z = 0.0;
@@ -1374,7 +778,11 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   }
   const int tok = resid_draw<In>(P, ctr, tc, trow, drow, kd, z,
                                  (double)P.u_rec[(int64_t)b * K1 + jr]);
-  if (lane == 0) P.out_token[b] = tok;
+  if (lane == 0) st_dev(P.out_token + b, tok);
+  if (P.hits) {
+    vm_complete();
+    hit_input_ready(P, b);
+  }
 }
 
 // ================================================================ k_write
@@ -1525,22 +933,23 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint8_t* p, size_t bytes) 
 // ================================================================ host side
 
 struct Layout {
-  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, cn, cpos, ctr, cnt, total;
+  size_t tm, ts, targ, dm, ds, darg, dtv, dti, rows, seqs, xd, yd, cn, cpos, cvm, ctr, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Candidate-list length of the statistics kernel for fan-out f: 4 covers
-// f <= 4, 16 covers the rest (the top-F contain the top-f).
+// Candidate-list length of the stream for fan-out f: 4 covers f <= 4, 16
+// covers the rest (the top-F contain the top-f).
 static int fork_F(int f) {
   if (f <= 0) return 0;
   return f <= 4 ? 4 : 16;
 }
 
-// Workspace layout for R row slots, B sequences and rows of cpr chunks.
+// Workspace layout for R row slots, B sequences and rows of cpr chunks,
+// after the control header (kCtlBytes, same offset for every call).
 static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   Layout L;
-  size_t o = 0;
+  size_t o = (size_t)kCtlBytes;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   const size_t RS = (size_t)(R * kMaxSeg);
   const size_t Fa = (size_t)(F > 0 ? F : 1);
@@ -1558,8 +967,8 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
   L.yd = take(sizeof(float) * R);
   L.cn = take(F > 0 ? sizeof(int) * RS : 0);
   L.cpos = take(F > 0 ? sizeof(int) * RS * kDumpCap : 0);
+  L.cvm = take(F > 0 ? sizeof(float) * RS * kDumpCap : 0);
   L.ctr = take(sizeof(double) * R * cpr);
-  L.cnt = take(sizeof(unsigned) * R * kCtrStride);
   L.total = o;
   return L;
 }
@@ -1567,6 +976,8 @@ static Layout make_layout(int64_t R, int64_t B, int64_t cpr, int F) {
 static Ws bind_ws(void* base, const Layout& L) {
   uint8_t* p = static_cast<uint8_t*>(base);
   Ws w;
+  w.seqctl = reinterpret_cast<unsigned*>(p);
+  w.rowctl = reinterpret_cast<unsigned*>(p + kMaxBatch * kSeqCtlBytes);
   w.tm = reinterpret_cast<float*>(p + L.tm);
   w.ts = reinterpret_cast<double*>(p + L.ts);
   w.targ = reinterpret_cast<int*>(p + L.targ);
@@ -1578,11 +989,11 @@ static Ws bind_ws(void* base, const Layout& L) {
   w.rows = reinterpret_cast<RowRec*>(p + L.rows);
   w.seqs = reinterpret_cast<SeqRec*>(p + L.seqs);
   w.xd = reinterpret_cast<float*>(p + L.xd);
+  w.yd = reinterpret_cast<float*>(p + L.yd);
   w.cn = reinterpret_cast<int*>(p + L.cn);
   w.cpos = reinterpret_cast<int*>(p + L.cpos);
-  w.yd = reinterpret_cast<float*>(p + L.yd);
+  w.cvm = reinterpret_cast<float*>(p + L.cvm);
   w.ctr = reinterpret_cast<double*>(p + L.ctr);
-  w.cnt = reinterpret_cast<unsigned*>(p + L.cnt);
   return w;
 }
 
@@ -1612,6 +1023,7 @@ static sv_status check_batch(const sv_batch* in, bool need_target, bool need_dra
   if (in->B < 0 || in->k < 1 || in->k > kMaxK || in->V < 2 || in->V > kMaxV)
     return SV_ERR_INVALID_ARG;
   if (in->dtype != SV_F32 && in->dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (in->B > kMaxBatch || (int64_t)in->B * (in->k + 1) > kMaxRows) return SV_ERR_INVALID_ARG;
   if (in->B == 0) return SV_OK;
   if (!in->temperature || !in->draft_tokens) return SV_ERR_INVALID_ARG;
   if (need_target) {
@@ -1658,8 +1070,8 @@ static int device_cus() {
   return v;
 }
 
-// Waves of k_stats<In, F> that fit on the device at once (occupancy query,
-// cached per instantiation and device).
+// Waves of a kernel that fit on the device at once (occupancy query,
+// cached per kernel and device).
 template <typename In, int F>
 static int64_t resident_waves() {
   static std::atomic<int64_t> cache[64];
@@ -1668,8 +1080,8 @@ static int64_t resident_waves() {
   int64_t v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)k_stats<In, F>, kBlock,
-                                                   0) != hipSuccess ||
+  const void* fn = (const void*)k_stats<In, F>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kBlock, 0) != hipSuccess ||
       blocks <= 0)
     blocks = 4;
   v = (int64_t)device_cus() * blocks * kWavesPerBlock;
@@ -1856,6 +1268,7 @@ sv_status sv_verify_ex(const sv_batch* in, const float* u_accept, const float* u
   P.p_draft = p_draft; P.q_draft = q_draft;
   P.fork_tok = forks ? forks->tokens : nullptr;
   P.fork_prob = forks ? forks->probs : nullptr;
+  P.hits = forks ? forks->hits : nullptr;
   P.nslots = (int64_t)in->B * (in->k + 1);
   P.ws = bind_ws(ws, make_layout(P.nslots, in->B, chunks_per_row(SV_F32, in->V), P.F));
   hipStream_t s = (hipStream_t)stream;
@@ -1867,11 +1280,6 @@ sv_status sv_verify_ex(const sv_batch* in, const float* u_accept, const float* u
     if (hipEventRecord((hipEvent_t)opts->ev_stats_end, s) != hipSuccess) return SV_ERR_HIP;
   }
   if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
-  if (forks && forks->hits) {
-    if (launch_hits(in->B, in->k, f, forks->tokens, accept_len, out_token, forks->hits, s) !=
-        hipSuccess)
-      return SV_ERR_HIP;
-  }
   return SV_OK;
 }
 
@@ -1907,7 +1315,7 @@ sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,
   hipStream_t s = (hipStream_t)stream;
   if (dispatch_stats(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
-  if (residual && dispatch_write(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
+  if (dispatch_write(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

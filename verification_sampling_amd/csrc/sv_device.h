@@ -391,4 +391,30 @@ __device__ __forceinline__ float wave_fth_largest(float x, int f) {
   return th;
 }
 
+// The f-th largest of the values the lanes hold (NV each; empty entries
+// hold -inf): -inf if fewer than f values exceed it.
+template <int NV>
+__device__ __forceinline__ float fth_largest_multi(const float (&x0)[NV], int f) {
+  float x[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) x[i] = x0[i];
+  float th = neg_inf();
+  for (int r = 0; r < f; ++r) {
+    float lm = x[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) lm = fmaxf(lm, x[i]);
+    th = wave_max(lm);
+    const unsigned long long m = __ballot(lm == th);
+    const int first = __ffsll((long long)m) - 1;
+    if (lane_id() == first) {
+      bool done = false;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (!done && x[i] == th) { x[i] = neg_inf(); done = true; }
+      }
+    }
+  }
+  return th;
+}
+
 }  // namespace sv

@@ -194,8 +194,10 @@ struct WaveStats {
 
 // Combines the lanes' sums relative to M = the largest lane reference; every
 // lane gets the result.  Lane terms are 2^(x c - hi_l); relative to M they
-// are multiplied by 2^(hi_l - M c): M c is split exactly (hm + lm) and the
-// 2^-lm factor applied in fp64.
+// are multiplied by 2^(hi_l - hm) with hm = M c rounded to fp32.  The sum
+// returned is relative to 2^hm: the exact M c = hm + lm (lm = fma(M, c,
+// -hm)), and the factor 2^-lm that makes it relative to M is applied by
+// whoever merges the partials (merge_scale), once per partial.
 __device__ __forceinline__ WaveStats wave_finish_warm(const Warm& a, float c) {
   WaveStats r;
   r.m = wave_max(a.r);
@@ -203,11 +205,19 @@ __device__ __forceinline__ WaveStats wave_finish_warm(const Warm& a, float c) {
   r.arg = kEmptyId;
   if (finitef(r.m)) {
     const float hm = r.m * c;
-    const float lm = fmaf(r.m, c, -hm);
     const double part = (a.s > 0.0) ? a.s * (double)__builtin_amdgcn_exp2f(a.hi - hm) : 0.0;
-    r.s = wave_sum(part) * exp2(-(double)lm);
+    r.s = wave_sum(part);
   }
   return r;
+}
+
+// The factor that turns a partial sum relative to 2^(m c rounded to fp32)
+// (wave_finish_warm) into one relative to the reference M >= m:
+// 2^((m - M) c - lm) with lm = fma(m, c, -m c), the rounding of m c.
+__device__ __forceinline__ double merge_scale(float m, float M, float c) {
+  const float hm = m * c;
+  const float lm = fmaf(m, c, -hm);
+  return exp2(((double)m - (double)M) * (double)c - (double)lm);
 }
 
 __device__ __forceinline__ WaveStats wave_finish_greedy(const Greedy& a) {
@@ -220,36 +230,45 @@ __device__ __forceinline__ WaveStats wave_finish_greedy(const Greedy& a) {
 
 // ---------------------------------------------------------------- forks
 // Fork candidates of a wave's segment of a row.  A vector is a candidate
-// when it may hold an element at or above the threshold kv (the F-th
-// largest lane maximum of the segment's first chunk, raised as better
-// candidates are found): at temperature > 0 when its sum of terms reaches
-// 2^(kv c - hi) (less a margin for rounding), at temperature 0 when its
-// maximum reaches kv.  A candidate lane appends the vector's element index
-// to its own slots in LDS; nothing else happens while streaming, so the
-// chunk's registers are free as soon as it is folded.  At the end of the
-// segment the positions are written out, compacted, for the decide kernel
-// to rank; the slots are reduced in the wave instead (vectors re-read,
-// elements ranked, the wave's top-F kept and kv raised) only if some lane
-// could overflow with the next chunk, or if the segment has more
-// candidates than its share of the output.
-constexpr int kCandSlots = 24;
+// when it may hold an element in the segment's top-f: in the segment's
+// first chunk, when its maximum reaches the threshold kv (the f-th largest
+// lane maximum of that chunk: at least f elements reach it, so no element
+// of the top-f lies below it); in later chunks, at temperature 0 when its
+// maximum exceeds kv (an element equal to kv there has a larger id than
+// the f elements that reach kv in the first chunk, so it cannot enter the
+// top-f), and at temperature > 0 when its sum of terms reaches
+// 2^(kv c - hi) (less a margin for rounding), which any element at or
+// above kv guarantees.  A candidate lane appends the vector's element index
+// and its maximum to its own slots in LDS; where the maximum was not
+// computed (later chunks at temperature > 0) the index is tagged in its low
+// bit (indices are multiples of the vector width) and the maximum left at
+// -inf.  Nothing else happens while streaming, so the chunk's registers
+// are free as soon as it is folded.  At the end of the segment the slots
+// are written out, compacted, for the row's ranking; they are reduced in
+// the wave instead (vectors re-read, elements ranked, the wave's top-F kept
+// and kv raised) only if some lane could overflow with the next chunk, or
+// if the segment has more candidates than its share of the output.
+constexpr int kCandSlots = 16;
+constexpr int kCandInexact = 1;  // tag bit of a candidate whose maximum is unknown
 
 template <int F>
 struct CandLds {
-  int pos[kCandSlots][kLanes];  // element index of each candidate vector
-  float wv[F > 0 ? F : 1];      // the wave's top-F so far (best first)
+  int pos[kCandSlots][kLanes];    // element index of each candidate vector (| tag)
+  float vm[kCandSlots][kLanes];   // its maximum, the drafted token masked (-inf if unknown)
+  float wv[F > 0 ? F : 1];        // the wave's top-F so far (best first)
   int wi[F > 0 ? F : 1];
 };
 
 // Appends vector u of this lane's chunk when bit u of `bits` is set.
 template <int F>
 __device__ __forceinline__ void cand_append(CandLds<F>* L, unsigned bits, int e_base, int slab,
-                                            int& nc) {
+                                            const float (&m8)[kU], bool exact, int& nc) {
   const int lane = lane_id();
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     if ((bits >> u) & 1u) {
-      L->pos[nc][lane] = e_base + u * slab;
+      L->pos[nc][lane] = (e_base + u * slab) | (exact ? 0 : kCandInexact);
+      L->vm[nc][lane] = m8[u];
       ++nc;
     }
   }
@@ -281,7 +300,7 @@ __device__ __forceinline__ void cand_reduce(CandLds<F>* L, const In* __restrict_
         v[q] = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
                           Elem<In>::kNegInfWord);
         if (i0 + q < nc) {
-          e0[q] = L->pos[i0 + q][lane];
+          e0[q] = L->pos[i0 + q][lane] & ~kCandInexact;
           load_vec<In>(row, e0[q], V, v[q]);
         }
       }
