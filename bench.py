@@ -22,6 +22,7 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -34,7 +35,7 @@ WORKLOAD = "batched_verify_fork_qwen"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stats_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "verification_sampling_amd", "csrc", n)
-                  for n in ("specverify.hip", "sv_device.h", "sv_stats.h")]
+                  for n in ("specverify.hip", "sv_device.h", "sv_stats.h", "sv_stream.h")]
 
 
 def parse():
@@ -153,20 +154,63 @@ def write_traffic(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
-def cpu_baseline(w, nseq):
-    """The oracle timed on the first nseq sequences; returns the baseline
-    record and the oracle's result (for the parity check)."""
+def _oracle_chunk(args):
+    """Worker of the multi-process oracle leg (runs in a fresh interpreter):
+    the oracle on a list of whole sequences."""
     import oracle
+    T, D, dtype, d, tau, ua, ur, f = args
+    r = oracle.verify_batch(T, D, dtype, d, tau, ua, ur, f=f)
+    return r.accept_len, r.token, r.fork_tokens
+
+
+def cpu_model():
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, nseq):
+    """The oracle timed on the first nseq sequences, on the host's cores.
+
+    Leg 1: one process (its result also serves the parity check).  Leg 2:
+    N = len(os.sched_getaffinity(0)) worker processes (fresh interpreters,
+    no GPU state), each taking a contiguous share of the sequences; the
+    workers' start-up is included.  The reported value is leg 2; cores is
+    the number of workers it actually used."""
+    import oracle
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
 
     seqs = list(range(min(nseq, w.B)))
     t0 = time.perf_counter()
     ref = oracle.verify_batch(w.target, w.draft, w.dtype, w.draft_tokens, w.temperature,
                               w.u_accept, w.u_recover, f=w.f, seqs=seqs)
-    dt = time.perf_counter() - t0
+    dt1 = time.perf_counter() - t0
     rows = len(seqs) * (w.k + 1)
-    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(seqs)} of {w.B} sequences of {WORKLOAD} "
-                      f"({rows} rows), one process, {dt:.1f} s"}, ref
+
+    ncpu = len(os.sched_getaffinity(0))
+    nw = max(1, min(ncpu, len(seqs)))
+    parts = [seqs[i * len(seqs) // nw:(i + 1) * len(seqs) // nw] for i in range(nw)]
+    jobs = [(w.target[p], w.draft[p], w.dtype, w.draft_tokens[p], w.temperature[p],
+             w.u_accept[p], w.u_recover[p], w.f) for p in parts if p]
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=len(jobs), mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_chunk, jobs))
+    dtn = time.perf_counter() - t0
+    import numpy as np
+    same = (np.array_equal(np.concatenate([r[0] for r in res]), ref.accept_len)
+            and np.array_equal(np.concatenate([r[1] for r in res]), ref.token))
+    return {"value": rows / dtn, "unit": "rows/s", "cores": len(jobs), "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cpus": ncpu,
+            "sample": f"{len(seqs)} of {w.B} sequences of {WORKLOAD} ({rows} rows): "
+                      f"{len(jobs)} worker processes, {dtn:.1f} s including their start-up",
+            "one_process": {"value": rows / dt1, "cores": 1, "seconds": dt1},
+            "legs_agree": bool(same)}, ref
 
 
 def parity(out, ref):
@@ -398,8 +442,18 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
 
+    # per-step times: the same calls with an event between consecutive steps
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    torch.cuda.synchronize()
+    pev[0].record()
+    for i in range(a.steps):
+        calls[i % 3]()
+        pev[i + 1].record()
+    torch.cuda.synchronize()
+    step_us = np.array([pev[i].elapsed_time(pev[i + 1]) * 1e3 for i in range(a.steps)])
+
     # the statistics kernel alone, from events the library records around it
-    # on the call's stream (a second pass of as many steps)
+    # on the call's stream (a further pass of as many steps)
     ev = [(hip.event(), hip.event()) for _ in range(a.steps)]
     opts = [sv.SvOpts(e0.value, e1.value) for e0, e1 in ev]
     torch.cuda.synchronize()
@@ -421,12 +475,24 @@ def main():
         if tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_launch")
 
-    if a.copy_calib:
-        x = torch.empty(total_bytes // 8, dtype=torch.float32, device=dev).normal_()
-        y = torch.empty_like(x)
-        for _ in range(3):
-            torch.neg(x, out=y)
-        torch.cuda.synchronize()
+    # what this GPU reaches on plain HBM traffic of the logits' size: a
+    # device-to-device copy (reads and writes every byte), three buffer sets
+    # rotated like the step
+    nbytes = stats_bytes // 16 * 16
+    srcs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(3)]
+    dsts = [torch.empty_like(srcs[0]) for _ in range(3)]
+    for i in range(3):
+        dsts[i].copy_(srcs[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(30):
+        dsts[i % 3].copy_(srcs[i % 3])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) * 1e-3 / 30
+    del srcs, dsts
+    copy_gbs = 2 * nbytes / copy_s / 1e9
 
     res = {
         "metric": METRIC,
@@ -448,8 +514,18 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_stats", "alg_bytes_per_launch": stats_bytes,
                      "avg_launch_us": stats_avg_s * 1e6},
-        "step_alg_GBs": total_bytes / (ms_per_step * 1e-3) / 1e9,
-        "step_frac_of_hbm_peak": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step": {"alg_bytes": total_bytes,
+                 "alg_GBs": total_bytes / (ms_per_step * 1e-3) / 1e9,
+                 "frac_of_hbm_peak": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "frac_of_measured_copy": total_bytes / (ms_per_step * 1e-3) / 1e9 / copy_gbs,
+                 "us_median": float(np.median(step_us)),
+                 "us_p10": float(np.percentile(step_us, 10)),
+                 "us_p90": float(np.percentile(step_us, 90)),
+                 "steps_with_events": int(a.steps)},
+        "measured_peak": {"d2d_copy_GBs": copy_gbs, "bytes": int(nbytes),
+                          "how": "device-to-device copy of a buffer of the step's logits "
+                                 "size (bytes read + bytes written per second), three sets "
+                                 "rotated"},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"], ref = cpu_baseline(w, a.cpu_seqs)

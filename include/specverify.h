@@ -5,10 +5,12 @@
  * C ABI.  No C++ or framework types cross it: plain pointers, sizes and the
  * small structs below.  Unless stated otherwise every array pointer is a
  * DEVICE pointer owned by the caller; the library allocates no memory of its
- * own, keeps no global mutable state, launches only on the stream it is
- * given (a hipStream_t passed as void*, NULL = the default stream) and
- * returns before the work completes: results are valid once the caller has
- * synchronised that stream.
+ * own, launches only on the stream it is given (a hipStream_t passed as
+ * void*, NULL = the default stream) and returns before the work completes:
+ * results are valid once the caller has synchronised that stream.  Its only
+ * process-wide state is a per-device cache of launch sizing (CU count and
+ * kernel occupancy, queried once per device and never changed afterwards);
+ * calls from several host threads are safe.
  *
  * What is computed (sources are cited by page title and section):
  *
@@ -34,7 +36,8 @@
  *    utilities file; f alternatives in the SSD README's benchmark commands,
  *    m.111cn.net translation, section 基准测试).
  *
- * Shapes and layout.  B sequences, k drafted positions (1 <= k <= 63),
+ * Shapes and layout.  B sequences (B <= 8192 and B * (k + 1) <= 32768 per
+ * call), k drafted positions (1 <= k <= 63),
  * positions j = 0..k where j = k is the bonus position, vocabulary
  * 2 <= V <= 1048576 shared by target and drafter (speculative-sampling page, "Quick Start &
  * Requirements": both models must share one vocabulary).  Logits are
@@ -59,13 +62,13 @@
  * in bounds).
  *
  * Workspace.  Every compute call takes a device workspace of at least
- * sv_workspace_size() bytes.  It must be zero-filled (sv_workspace_init, or
- * any zero fill) before its first use, and again before a call whose entry
- * point or sizes (B, k, V, f; rows for sv_softmax_temp) differ from those of
- * the previous call on it: where its arrival counters sit depends on them.
- * A call leaves the workspace ready for the next call of the same kind.
- * Calls that share a workspace must not overlap in time (use one workspace
- * per stream).
+ * sv_workspace_size() bytes.  It must be zero-filled once, before its first
+ * use (sv_workspace_init, or any zero fill).  Its arrival counters sit in a
+ * control header at its start, at offsets that depend on no size, and every
+ * call that runs to completion returns them to zero, so one workspace then
+ * serves any sequence of calls of any entry point and any sizes.  Calls
+ * that share a workspace must not overlap in time (use one workspace per
+ * stream).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -133,7 +136,8 @@ typedef struct sv_opts {
 size_t sv_workspace_size(int32_t B, int32_t k, int32_t V, int32_t f);
 
 /* Zero-fills `bytes` bytes of a workspace on `stream` with a fill kernel
- * (no memset node, so it can be captured in a graph). */
+ * (no memset node, so it can be captured in a graph).  Needed once per
+ * workspace, before its first use. */
 sv_status sv_workspace_init(void* ws, size_t bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
@@ -142,7 +146,11 @@ const char* sv_status_string(int32_t status);
 /* Library version string (static storage). */
 const char* sv_version(void);
 
-/* Temperature softmax of `rows` logits rows:
+/* Temperature softmax of `rows` logits rows, the p and q of the
+ * speculative-sampling rule at the sequence's temperature (the sampler's
+ * temperature, tanishqkumar/ssd repository summary, highlighted sampler
+ * file; the rule itself: "How It Works", speculative-sampling project
+ * page):
  * probs[r][t] = softmax(logits[r] / tau)[t] with tau = temperature[r /
  * rows_per_temp]; one-hot at the first maximum when tau = 0.  logits: rows
  * of V elements at row_stride elements; probs: fp32 rows at out_row_stride
@@ -155,8 +163,13 @@ sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows,
                           float* probs, int64_t out_row_stride, void* ws,
                           size_t ws_bytes, void* stream);
 
-/* The verify step, with the forked recovery tokens fused into the same pass
- * over the draft logits when `forks` is non-NULL.
+/* The verify step ("How It Works", speculative-sampling project page; the
+ * target checks all drafted tokens in one pass and keeps the accepted
+ * prefix, "What changes in SSD", hysenlabs.com editorial): acceptance tests
+ * u < min(1, p/q), first rejection, and the recovery or bonus draw, with the
+ * forked recovery tokens (async-SD utilities file, tanishqkumar/ssd
+ * repository summary) fused into the same pass over the draft logits when
+ * `forks` is non-NULL.
  *   u_accept [B][k]    uniform of the acceptance test at each position
  *   u_recover [B][k+1] uniform of the draw at the outcome position n
  *   accept_len [B]     out: n = number of accepted drafted tokens, in [0, k]
@@ -167,9 +180,9 @@ sv_status sv_softmax_temp(const void* logits, int32_t dtype, int64_t rows,
  * Launches: a streaming statistics kernel (one resident round of waves,
  * each over an equal slab range of one row, writing per-range partials),
  * then a decision kernel that merges the partials per row, decides each
- * sequence, ranks the forks, and re-reads only row n of the temperature > 0
- * sequences for the draw; with forks->hits, then the lookup of
- * sv_cache_hit. */
+ * sequence, ranks the forks, re-reads only row n of the temperature > 0
+ * sequences for the draw and, with forks->hits, writes the lookup of
+ * sv_cache_hit once the token and the forks are in (no third launch). */
 sv_status sv_verify(const sv_batch* in, const float* u_accept,
                     const float* u_recover, int32_t* accept_len,
                     int32_t* out_token, float* p_draft, float* q_draft,
@@ -184,7 +197,10 @@ sv_status sv_verify_ex(const sv_batch* in, const float* u_accept,
                        void* stream, const sv_opts* opts);
 
 /* The draw at a given position of each sequence, and optionally the full
- * residual distributions.
+ * residual distributions: the regeneration from the first divergence of
+ * "How It Works" (speculative-sampling project page), from the normalised
+ * residual max(0, p_n - q_n) whose use keeps the output law the target's
+ * ("What changes in SSD", hysenlabs.com editorial).
  *   position [B]   n in [0, k]: n < k draws from max(0, p_n - q_n)
  *                  normalised (p_n if that is zero everywhere), n = k draws
  *                  the bonus token from p_k; greedy at temperature 0
@@ -200,9 +216,13 @@ sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,
                              int64_t res_row_stride, void* ws,
                              size_t ws_bytes, void* stream);
 
-/* Forked recovery tokens alone, from the draft logits only (drafter-side
+/* Forked recovery tokens alone, from the draft logits only: the top-f
+ * tokens per position with the drafted token masked (async-SD utilities
+ * file, tanishqkumar/ssd repository summary; f alternatives per position,
+ * SSD README translation, m.111cn.net, section 基准测试), for drafter-side
  * use in SSD, where the drafter runs on its own device without the target's
- * logits).  in->target may be NULL. */
+ * logits ("What changes in SSD", hysenlabs.com editorial).  in->target may
+ * be NULL. */
 sv_status sv_forked_topf(const sv_batch* in, const sv_forks* forks, void* ws,
                          size_t ws_bytes, void* stream);
 

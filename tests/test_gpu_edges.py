@@ -272,8 +272,7 @@ def test_cache_hit_on_drafter_forks(sv):
 
 def test_workspace_reused_across_shapes(sv):
     """One workspace serves calls of different sizes and entry points in
-    turn: the arrival counters move with the sizes, and every call must find
-    its own zeroed."""
+    turn (grown, and zero-filled, only when a call needs more room)."""
     ws = sv.Workspace(torch.device("cuda", 0))
     shapes = [(2, 5, 33, 5, "bf16"), (6, 7, 3000, 3, "bf16"), (1, 2, 17, 0, "f32"),
               (2, 5, 33, 5, "bf16"), (9, 3, 4097, 2, "f32"), (6, 7, 3000, 3, "bf16")]
@@ -295,6 +294,45 @@ def test_workspace_reused_across_shapes(sv):
             torch.cuda.synchronize()
             assert torch.equal(toks, out["fork_tokens"])
     log("[edges] workspace reused across shapes and entry points: ok")
+
+
+def test_workspace_zeroed_once_serves_every_call(sv):
+    """The workspace contract: zero-filled once, then any sequence of calls
+    of any entry point and size, with no re-initialisation in between, gives
+    the oracle's results (the arrival counters sit at fixed offsets and every
+    call returns them to zero)."""
+    shapes = [(2, 5, 33, 5, "bf16"), (6, 7, 3000, 3, "bf16"), (1, 2, 17, 0, "f32"),
+              (9, 3, 4097, 2, "f32"), (64, 7, 2048, 3, "bf16")]
+    need = max(sv.workspace_size(B, k, V, f) for B, k, V, f, _ in shapes)
+    need = max(need, sv.workspace_size(40, 0, 4097, 0))
+    ws = sv.Workspace(torch.device("cuda", 0))
+    buf = ws.get(need)                        # the one zero fill
+    for rnd in range(2):
+        for i, (B, k, V, f, dtype) in enumerate(shapes):
+            w = synth(B, k, V, dtype, 0.9, seed=5100 + i, f=f)
+            T, D = padded_dev(w.target, dtype), padded_dev(w.draft, dtype)
+            d = torch.from_numpy(w.draft_tokens).cuda()
+            tau = torch.from_numpy(w.temperature).cuda()
+            out = sv.verify(T, D, d, tau, torch.from_numpy(w.u_accept).cuda(),
+                            torch.from_numpy(w.u_recover).cuda(), f=f, want_p=True, want_q=True,
+                            want_hits=f > 0, workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.verify_batch(w.target, w.draft, dtype, w.draft_tokens, w.temperature,
+                                      w.u_accept, w.u_recover, f=f)
+            compare_verify(out, ref, np.arange(B), f, k)
+            if f > 0:
+                toks, _ = sv.forked_topf(D, d, tau, f, workspace=ws)
+                torch.cuda.synchronize()
+                assert torch.equal(toks, out["fork_tokens"])
+            host_rows = w.target.reshape(-1, V)[:40]
+            rows = padded_dev(host_rows[None], dtype)[0]   # aligned rows, [n, V]
+            tr = torch.full((rows.shape[0],), 0.8, dtype=torch.float32, device="cuda")
+            pr = sv.softmax_temp(rows, tr, workspace=ws)
+            torch.cuda.synchronize()
+            refp = oracle.softmax_rows(host_rows, dtype, np.full(rows.shape[0], 0.8))
+            assert_probs_close(pr.cpu().numpy(), refp, "softmax rows")
+            assert ws.buf is buf, "the workspace was reallocated"
+    log("[edges] workspace zeroed once serves every call: ok")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

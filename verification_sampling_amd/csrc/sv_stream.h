@@ -31,7 +31,7 @@ enum Mode : int { kVerify = 0, kForks = 1, kResidual = 2, kSoftmax = 3 };
 constexpr int kMaxChunks = 1024;
 constexpr int64_t kMaxV = (int64_t)kMaxChunks * kU * kLanes * 4;
 constexpr int kMaxSeg = 64;   // partials per row (one lane each when merged)
-constexpr int kDumpCap = 64;  // fork candidate vectors a segment passes on
+constexpr int kDumpCap = 128;  // fork candidate vectors a segment passes on
 
 // ---------------------------------------------------------------- control
 // The arrival counters sit in a control header at the start of every
@@ -248,7 +248,7 @@ struct WaveState {
 template <typename In>
 __device__ __forceinline__ void capture(const uint4 (&raw)[kU], int e_base, int id, float* out) {
   const float2 r = pick_elem<In>(raw[0], raw[1], raw[2], raw[3], e_base, id);
-  if (r.y != 0.0f) st_dev(out, r.x);
+  if (r.y != 0.0f) *out = r.x;
 }
 
 // One chunk of a segment, already in registers.  RT / RD: the target / draft
@@ -374,9 +374,8 @@ __device__ __forceinline__ void stats_segment(const RowPlan& pl, int V, const In
 // (reference or maximum, fp64 sum, argmax) for each tensor read, the
 // drafted token's logits when the segment holds it, and the draft's fork
 // candidates (positions and vector maxima, compacted, with the list of any
-// in-wave reduction).  One wave; L is the wave's own LDS slots.  Every
-// store is device-scope, so a wave of the same launch on another XCD can
-// read the results once the arrival that follows has been counted.
+// in-wave reduction), read by the next launch.  One wave; L is the wave's
+// own LDS slots.
 template <typename In, int F>
 __device__ __forceinline__ void stream_segment(const Params& P, int64_t slot, int b, int j,
                                                int seg, int nparts, CandLds<F>* L) {
@@ -431,24 +430,24 @@ __device__ __forceinline__ void stream_segment(const Params& P, int64_t slot, in
       int* dst = W.cpos + part * kDumpCap + (incl - st.nc);
       float* dvm = W.cvm + part * kDumpCap + (incl - st.nc);
       for (int i = 0; i < st.nc; ++i) {
-        st_dev(dst + i, L->pos[i][lane]);
-        st_dev(dvm + i, L->vm[i][lane]);
+        dst[i] = L->pos[i][lane];
+        dvm[i] = L->vm[i][lane];
       }
-      if (lane == 0) st_dev(W.cn + part, total);
+      if (lane == 0) W.cn[part] = total;
     }
   }
 
   if (pl.readT) {
     const WaveStats ws = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
-    if (lane == 0) { st_dev(W.tm + part, ws.m); st_dev(W.ts + part, ws.s); st_dev(W.targ + part, ws.arg); }
+    if (lane == 0) { W.tm[part] = ws.m; W.ts[part] = ws.s; W.targ[part] = ws.arg; }
   }
   if (pl.readD) {
     const WaveStats ws = pl.greedy ? wave_finish_greedy(st.dg) : wave_finish_warm(st.dw, c);
-    if (lane == 0) { st_dev(W.dm + part, ws.m); st_dev(W.ds + part, ws.s); st_dev(W.darg + part, ws.arg); }
+    if (lane == 0) { W.dm[part] = ws.m; W.ds[part] = ws.s; W.darg[part] = ws.arg; }
     if constexpr (F > 0) {
       if (pl.topf && lane < F) {
-        st_dev(W.dtv + part * F + lane, L->wv[lane]);
-        st_dev(W.dti + part * F + lane, L->wi[lane]);
+        W.dtv[part * F + lane] = L->wv[lane];
+        W.dti[part * F + lane] = L->wi[lane];
       }
     }
   }

@@ -122,26 +122,21 @@ def _stream_handle(stream=None):
 # ------------------------------------------------------------------ workspace
 
 class Workspace:
-    """A device buffer for the library's scratch data.  Each call leaves it
-    ready for the next call of the same kind (entry point and sizes); the
-    counters it holds move with the sizes, so the buffer is zero-filled again
-    whenever the kind changes.  Calls sharing it must not overlap (one
-    workspace per stream)."""
+    """A device buffer for the library's scratch data, zero-filled once when
+    it is allocated (or grown); every call leaves its counters at zero, so
+    the buffer then serves calls of any entry point and size.  Calls sharing
+    it must not overlap (one workspace per stream)."""
 
     def __init__(self, device=None):
         self.device = torch.device("cuda") if device is None else torch.device(device)
         self.buf = None
-        self.kind = None
 
     def get(self, nbytes: int, kind=None, stream=None) -> torch.Tensor:
-        fresh = self.buf is None or self.buf.numel() < nbytes
-        if fresh:
+        if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
                                    device=self.device)
-        if fresh or kind != self.kind:
             _check(lib().sv_workspace_init(_ptr(self.buf), self.buf.numel(),
                                            _stream_handle(stream)), "sv_workspace_init")
-        self.kind = kind
         return self.buf
 
 
