@@ -1138,6 +1138,7 @@ static hipError_t launch_write(const Params& P, hipStream_t s) {
   const int64_t nslots = (P.mode == kSoftmax) ? P.nslots : (int64_t)P.B * (P.k + 1);
   const int64_t waves = nslots * P.cpr;
   if (waves == 0) return hipSuccess;
+  if (!P.out) return hipErrorInvalidValue;  // every wave stores into the output rows
   hipLaunchKernelGGL((k_write<In>), grid_for(waves), dim3(kBlock), 0, s, P);
   return hipGetLastError();
 }
@@ -1315,7 +1316,9 @@ sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,
   hipStream_t s = (hipStream_t)stream;
   if (dispatch_stats(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   if (dispatch_decide(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
-  if (dispatch_write(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
+  // the distributions are written only when asked for (the token-only call
+  // has no output rows)
+  if (residual && dispatch_write(in->dtype, P, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

@@ -530,8 +530,12 @@ __device__ __forceinline__ ResidCoef resid_coef(float tm, double ts, float dm, d
   return k;
 }
 
+// p and q are each rounded to fp32 before the difference is taken (no
+// contraction of a product into the subtraction), so that equal target and
+// draft rows give a residual of exactly zero.
 __device__ __forceinline__ void resid_elem(const ResidCoef& k, float x, float y, float& p,
                                            float& r) {
+#pragma clang fp contract(off)
   p = __builtin_amdgcn_exp2f(fmaf(x, k.c, -k.thi)) * k.tscale;
   if (k.has_q) {
     const float q = __builtin_amdgcn_exp2f(fmaf(y, k.c, -k.dhi)) * k.dscale;
