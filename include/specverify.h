@@ -5,12 +5,15 @@
  * C ABI.  No C++ or framework types cross it: plain pointers, sizes and the
  * small structs below.  Unless stated otherwise every array pointer is a
  * DEVICE pointer owned by the caller; the library allocates no memory of its
- * own, launches only on the stream it is given (a hipStream_t passed as
+ * own (sv_verify_noalloc aside, whose workspace is a static device array),
+ * launches only on the stream it is given (a hipStream_t passed as
  * void*, NULL = the default stream) and returns before the work completes:
- * results are valid once the caller has synchronised that stream.  Its only
+ * results are valid once the caller has synchronised that stream.  Its
  * process-wide state is a per-device cache of launch sizing (CU count and
- * kernel occupancy, queried once per device and never changed afterwards);
- * calls from several host threads are safe.
+ * kernel occupancy, queried once per device and never changed afterwards)
+ * and, for sv_verify_noalloc only, that array and its address on each
+ * device; calls from several host threads are safe (sv_verify_noalloc's
+ * calls on one device share its array: see there).
  *
  * What is computed (sources are cited by page title and section):
  *
@@ -195,6 +198,30 @@ sv_status sv_verify_ex(const sv_batch* in, const float* u_accept,
                        int32_t* out_token, float* p_draft, float* q_draft,
                        const sv_forks* forks, void* ws, size_t ws_bytes,
                        void* stream, const sv_opts* opts);
+
+/* Bytes of the static scratch array of sv_verify_noalloc, on each device it
+ * runs on (enough for B = 64, k = 7, V = 151936, f <= 16). */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* sv_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  Same
+ * arguments, outputs, launches and results as sv_verify, bitwise, without
+ * the workspace arguments: the workspace is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES, one per device, held from the first call on a
+ * device until the process ends.  The call allocates and frees nothing.
+ *   Returns SV_ERR_WORKSPACE, launching nothing, when the shape needs more
+ *   than that (sv_workspace_size(B, k, V, f) > SV_NOALLOC_SCRATCH_BYTES).
+ *   The first call on a device looks up the array's address with that
+ *   device current and zero-fills the array on `stream` (one extra launch);
+ *   make that first call outside a graph capture.  Every call on a device
+ *   uses the same array and leaves its contents behind: calls on one device
+ *   that may overlap in time (several streams, several threads) race and
+ *   must be serialised by the caller, for example by issuing them all on
+ *   one stream. */
+sv_status sv_verify_noalloc(const sv_batch* in, const float* u_accept,
+                            const float* u_recover, int32_t* accept_len,
+                            int32_t* out_token, float* p_draft, float* q_draft,
+                            const sv_forks* forks, void* stream);
 
 /* The draw at a given position of each sequence, and optionally the full
  * residual distributions: the regeneration from the first divergence of

@@ -163,3 +163,29 @@ def test_sample_temp_validation(L):
     assert call(logits=ctypes.c_void_p(FAKE + 8)) == MISALIGNED
     for name in ("logits", "temp", "u", "out"):
         assert call(**{name: None}) == INVALID
+
+
+def test_noalloc_scratch_limit_and_validation(L):
+    """sv_verify_noalloc refuses shapes whose workspace exceeds its static
+    array, and bad arguments, before any GPU call; the binding's copy of the
+    array's size is the header's."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+SV_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m, "SV_NOALLOC_SCRATCH_BYTES not found in the header"
+    assert sv.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    p = ctypes.c_void_p(FAKE)
+
+    def call(b, forks=None):
+        return L.sv_verify_noalloc(ctypes.byref(b) if b is not None else None, p, p, p, p, None,
+                                   None, ctypes.byref(forks) if forks else None, None)
+
+    assert call(None) == INVALID
+    assert call(batch(k=64)) == INVALID
+    assert call(batch(V=1)) == INVALID
+    assert call(batch(), forks=sv.SvForks(17, FAKE, FAKE)) == INVALID
+    assert call(batch(), forks=sv.SvForks(0, FAKE, FAKE)) == INVALID
+    big = batch(B=256, k=7, V=151936, t_row=151936, d_row=151936)
+    assert L.sv_workspace_size(256, 7, 151936, 3) > sv.NOALLOC_SCRATCH_BYTES
+    assert call(big, forks=sv.SvForks(3, FAKE, FAKE)) == WORKSPACE
+    # the headline batch fits
+    assert L.sv_workspace_size(64, 7, 151936, 16) <= sv.NOALLOC_SCRATCH_BYTES

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -1182,6 +1183,47 @@ static sv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 using namespace sv;
 
+// ================================================================ scratch
+// The workspace of sv_verify_noalloc: one array per device, in the code
+// object's zero-initialised data, held until the process ends.  Host code
+// never passes the array's name to a kernel or a copy (on the host it is
+// only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) uint8_t scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[kMaxDevices];  // the array's address on each device
+}  // namespace
+
+// The current device's scratch address.  The first call on a device looks
+// it up (with that device current) and zero-fills the array on `stream`, so
+// that the arrival counters at its start begin at zero; later calls reuse
+// both.
+static sv_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* a = nullptr;
+      if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return SV_ERR_HIP;
+      const size_t n16 = SV_NOALLOC_SCRATCH_BYTES / 16;
+      const unsigned blocks = (unsigned)std::min<size_t>((n16 + kBlock - 1) / kBlock, 4096);
+      hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(kBlock), 0, stream, (uint8_t*)a,
+                         (size_t)SV_NOALLOC_SCRATCH_BYTES);
+      if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+      p = a;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SV_OK;
+}
+
 extern "C" {
 
 size_t sv_workspace_size(int32_t B, int32_t k, int32_t V, int32_t f) {
@@ -1289,6 +1331,22 @@ sv_status sv_verify(const sv_batch* in, const float* u_accept, const float* u_re
                     const sv_forks* forks, void* ws, size_t ws_bytes, void* stream) {
   return sv_verify_ex(in, u_accept, u_recover, accept_len, out_token, p_draft, q_draft, forks,
                       ws, ws_bytes, stream, nullptr);
+}
+
+sv_status sv_verify_noalloc(const sv_batch* in, const float* u_accept, const float* u_recover,
+                            int32_t* accept_len, int32_t* out_token, float* p_draft,
+                            float* q_draft, const sv_forks* forks, void* stream) {
+  if (!in) return SV_ERR_INVALID_ARG;
+  const int f = forks ? forks->f : 0;
+  if (forks && (f < 1 || f > kMaxF)) return SV_ERR_INVALID_ARG;
+  const size_t need = sv_workspace_size(in->B, in->k, in->V, f);
+  if (need == 0) return SV_ERR_INVALID_ARG;
+  if (need > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const sv_status st = scratch_address((hipStream_t)stream, &ws);
+  if (st != SV_OK) return st;
+  return sv_verify_ex(in, u_accept, u_recover, accept_len, out_token, p_draft, q_draft, forks, ws,
+                      (size_t)SV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 sv_status sv_residual_sample(const sv_batch* in, const int32_t* position,

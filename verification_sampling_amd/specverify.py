@@ -81,6 +81,8 @@ def lib():
             L.sv_verify.restype = i32
             L.sv_verify_ex.argtypes = [pb, vp, vp, vp, vp, vp, vp, pf, vp, sz, vp, po]
             L.sv_verify_ex.restype = i32
+            L.sv_verify_noalloc.argtypes = [pb, vp, vp, vp, vp, vp, vp, pf, vp]
+            L.sv_verify_noalloc.restype = i32
             L.sv_residual_sample.argtypes = [pb, vp, vp, vp, vp, i64, i64, vp, sz, vp]
             L.sv_residual_sample.restype = i32
             L.sv_forked_topf.argtypes = [pb, pf, vp, sz, vp]
@@ -235,6 +237,27 @@ def _out(t, shape, dtype, name):
 
 # ------------------------------------------------------------------ API
 
+def _verify_outputs(out, B, k, f):
+    _out(out.get("accept_len"), (B,), torch.int32, "accept_len")
+    _out(out.get("out_token"), (B,), torch.int32, "out_token")
+    for name in ("p_draft", "q_draft"):
+        if out.get(name) is not None:
+            _out(out[name], (B, k), torch.float32, name)
+    if f > 0:
+        _out(out.get("fork_tokens"), (B, k + 1, f), torch.int32, "fork_tokens")
+        _out(out.get("fork_probs"), (B, k + 1, f), torch.float32, "fork_probs")
+        if out.get("cache_hit") is not None:
+            _out(out["cache_hit"], (B,), torch.int32, "cache_hit")
+
+
+def _forks_of(out, f):
+    if f <= 0:
+        return None
+    hits = out.get("cache_hit")
+    return SvForks(int(f), out["fork_tokens"].data_ptr(), out["fork_probs"].data_ptr(),
+                   hits.data_ptr() if hits is not None else None)
+
+
 def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int = 0,
            want_p: bool = False, want_q: bool = False, want_hits: bool = False,
            workspace: Optional[Workspace] = None, stream=None, out=None, timing_events=None):
@@ -254,16 +277,7 @@ def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int
     _f32(u_accept, (B, k), "u_accept")
     _f32(u_recover, (B, k + 1), "u_recover")
     if out is not None:
-        _out(out.get("accept_len"), (B,), torch.int32, "accept_len")
-        _out(out.get("out_token"), (B,), torch.int32, "out_token")
-        for name in ("p_draft", "q_draft"):
-            if out.get(name) is not None:
-                _out(out[name], (B, k), torch.float32, name)
-        if f > 0:
-            _out(out.get("fork_tokens"), (B, k + 1, f), torch.int32, "fork_tokens")
-            _out(out.get("fork_probs"), (B, k + 1, f), torch.float32, "fork_probs")
-            if out.get("cache_hit") is not None:
-                _out(out["cache_hit"], (B,), torch.int32, "cache_hit")
+        _verify_outputs(out, B, k, f)
     dev = _same_device([target, draft, draft_tokens, temperature, u_accept, u_recover]
                        + ([t for t in out.values() if t is not None] if out else []), "verify")
     if out is None:
@@ -280,11 +294,7 @@ def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int
             out["fork_probs"] = torch.empty(B, k + 1, f, dtype=torch.float32, device=dev)
             if want_hits:
                 out["cache_hit"] = torch.empty(B, dtype=torch.int32, device=dev)
-    forks = None
-    if f > 0:
-        hits = out.get("cache_hit")
-        forks = SvForks(int(f), out["fork_tokens"].data_ptr(), out["fork_probs"].data_ptr(),
-                        hits.data_ptr() if hits is not None else None)
+    forks = _forks_of(out, f)
     ws = workspace or default_workspace(dev, stream)
     buf = ws.get(workspace_size(B, k, b.V, f), ("verify", B, k, b.V, f), stream)
     opts = None
@@ -297,6 +307,49 @@ def verify(target, draft, draft_tokens, temperature, u_accept, u_recover, f: int
         _ptr(buf), buf.numel(), _stream_handle(stream),
         ctypes.byref(opts) if opts is not None else None)
     _check(code, "sv_verify")
+    return out
+
+
+# Bytes of sv_verify_noalloc's static scratch array (the header's
+# SV_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def verify_noalloc(target, draft, draft_tokens, temperature, u_accept, u_recover, out,
+                   f: int = 0, stream=None):
+    """sv_verify_noalloc: sv_verify into the caller's output tensors (the
+    dict keys of verify(); accept_len and out_token required, p_draft,
+    q_draft optional, fork_tokens and fork_probs required when f > 0,
+    cache_hit optional), with the library's static scratch array as the
+    workspace.  Allocates nothing.  Calls on one device share that array:
+    issue them on one stream."""
+    if target is None:
+        raise ValueError("verify_noalloc needs the target logits")
+    if out is None:
+        raise ValueError("verify_noalloc writes into `out`, which must hold the output tensors")
+    f = int(f)
+    if f < 0:
+        raise ValueError("f must be >= 0")
+    b = _batch(target, draft, draft_tokens, temperature, forks=f > 0)
+    B, k = b.B, b.k
+    if f > min(16, b.V - 1):
+        raise ValueError("f must be at most min(16, V - 1)")
+    _f32(u_accept, (B, k), "u_accept")
+    _f32(u_recover, (B, k + 1), "u_recover")
+    _verify_outputs(out, B, k, f)
+    _same_device([target, draft, draft_tokens, temperature, u_accept, u_recover]
+                 + [t for t in out.values() if t is not None], "verify_noalloc")
+    need = workspace_size(B, k, b.V, f)
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise SpecVerifyError(
+            f"sv_verify_noalloc: B={B}, k={k}, V={b.V}, f={f} needs {need} bytes of workspace, "
+            f"more than its scratch array of {NOALLOC_SCRATCH_BYTES} bytes; use verify()")
+    forks = _forks_of(out, f)
+    code = lib().sv_verify_noalloc(
+        ctypes.byref(b), _ptr(u_accept), _ptr(u_recover), _ptr(out["accept_len"]),
+        _ptr(out["out_token"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+        ctypes.byref(forks) if forks is not None else None, _stream_handle(stream))
+    _check(code, "sv_verify_noalloc")
     return out
 
 
