@@ -124,13 +124,12 @@ __device__ __noinline__ WarmFix warm_redo(uint4 v0, uint4 v1, uint4 v2, uint4 v3
   return w;
 }
 
-// Folds one chunk into the lane's sum and returns the chunk's sum of terms;
-// vs gets the per-vector sums.  On the segment's first chunk the reference
-// is first set to the lane's maximum of that chunk (m8 then holds the vector
-// maxima).  Every lane must call it (it contains a wave-uniform branch).
+// The chunk's sums of terms (per vector in vs, and the total), before the
+// overflow check.  On the segment's first chunk the reference is first set
+// to the lane's maximum of that chunk (m8 then holds the vector maxima).
 template <typename In, bool FIRST>
-__device__ __forceinline__ float warm_fold_vs(Warm& a, const uint4 (&raw)[kU], float c,
-                                              float (&m8)[kU], float (&vs)[kU]) {
+__device__ __forceinline__ float warm_terms(Warm& a, const uint4 (&raw)[kU], float c,
+                                            float (&m8)[kU], float (&vs)[kU]) {
   if constexpr (FIRST) {
     const float mc = vec_maxima<In>(raw, m8);
     if (mc > neg_inf()) {
@@ -138,18 +137,38 @@ __device__ __forceinline__ float warm_fold_vs(Warm& a, const uint4 (&raw)[kU], f
       a.hi = mc * c;
     }
   }
-  float sc = exp_sums<In>(raw, c, a.hi, vs);
-  const bool redo = !(sc < pos_inf());  // overflow, or no reference yet
-  if (__ballot(redo)) {
-    if (redo) {
-      const WarmFix w = warm_redo<In>(raw[0], raw[1], raw[2], raw[3], a.r, a.hi, a.s, c);
-      a.r = w.r;
-      a.hi = w.hi;
-      a.s = w.s;
-      sc = w.sc;
+  return exp_sums<In>(raw, c, a.hi, vs);
+}
+
+__device__ __forceinline__ bool warm_overflow(float sc) { return !(sc < pos_inf()); }
+
+// A lane whose chunk overflowed (or that had no reference yet): the
+// reference is raised and the chunk recomputed (sc, vs replaced).
+template <typename In>
+__device__ __forceinline__ void warm_fix(Warm& a, const uint4 (&raw)[kU], float c, float& sc,
+                                         float (&vs)[kU]) {
+  const WarmFix w = warm_redo<In>(raw[0], raw[1], raw[2], raw[3], a.r, a.hi, a.s, c);
+  a.r = w.r;
+  a.hi = w.hi;
+  a.s = w.s;
+  sc = w.sc;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) vs[u] = w.vs[u];
-    }
+  for (int u = 0; u < kU; ++u) vs[u] = w.vs[u];
+}
+
+// Folds one chunk into the lane's sum and returns the chunk's sum of terms;
+// vs gets the per-vector sums and `fixed` whether some lane's reference was
+// raised (wave-uniform).  Every lane must call it (it contains a
+// wave-uniform branch).
+template <typename In, bool FIRST>
+__device__ __forceinline__ float warm_fold_vs(Warm& a, const uint4 (&raw)[kU], float c,
+                                              float (&m8)[kU], float (&vs)[kU], bool& fixed) {
+  float sc = warm_terms<In, FIRST>(a, raw, c, m8, vs);
+  const bool redo = warm_overflow(sc);
+  fixed = false;
+  if (__ballot(redo)) {
+    fixed = true;
+    if (redo) warm_fix<In>(a, raw, c, sc, vs);
   }
   a.s += (double)sc;
   return sc;
@@ -159,7 +178,8 @@ template <typename In, bool FIRST>
 __device__ __forceinline__ float warm_fold(Warm& a, const uint4 (&raw)[kU], float c,
                                            float (&m8)[kU]) {
   float vs[kU];
-  return warm_fold_vs<In, FIRST>(a, raw, c, m8, vs);
+  bool fixed;
+  return warm_fold_vs<In, FIRST>(a, raw, c, m8, vs, fixed);
 }
 
 // Temperature 0: running maximum, and the lowest id holding it.  e_base is

@@ -242,7 +242,13 @@ struct WaveState {
   Greedy tg, dg;  // temperature 0
   int nc;         // fork candidate slots in use (this lane)
   float kv;       // fork candidate threshold (wave-uniform)
+  float eth;      // this lane's term of an element at kv, 2^(kv c - hi), less a margin
 };
+
+// Recomputes st.eth after kv or the draft reference changed.
+__device__ __forceinline__ void refresh_eth(WaveState& st, float c) {
+  st.eth = __builtin_amdgcn_exp2f(fmaf(st.kv, c, -st.dw.hi)) * 0.999999f;
+}
 
 // Writes element id of a chunk (held by one lane, if any) to *out.
 template <typename In>
@@ -267,9 +273,6 @@ __device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* 
   const bool has_d = pl.d_id >= cs && pl.d_id < cs + nv * SLAB;
   if constexpr (RT) {
     if (has_d) capture<In>(traw, e_base, pl.d_id, xd);
-    float m8[kU];
-    if constexpr (GREEDY) greedy_fold<In>(st.tg, traw, e_base, true, m8);
-    else warm_fold<In, FIRST>(st.tw, traw, c, m8);
   }
   if constexpr (RD) {
     if (has_d) capture<In>(draw, e_base, pl.d_id, yd);
@@ -278,49 +281,65 @@ __device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* 
 #pragma unroll
       for (int u = 0; u < kU; ++u) draw[u] = m.v[u];
     }
-    float m8[kU], vs[kU];
-    // at temperature 0 the (masked) argmax is kept too: with forks it gives
-    // the unmasked argmax together with the drafted token's logit
+  }
+  // fold: running maxima at temperature 0 (with forks the draft's (masked)
+  // argmax is kept too: it gives the unmasked argmax together with the
+  // drafted token's logit), sums of terms above it
+  float m8[kU], vs[kU];  // the draft chunk's vector maxima and sums of terms
+  bool d_fixed = false;  // some draft lane's reference was raised
+  if constexpr (RT) {
+    float m8t[kU];
+    if constexpr (GREEDY) greedy_fold<In>(st.tg, traw, e_base, true, m8t);
+    else warm_fold<In, FIRST>(st.tw, traw, c, m8t);
+  }
+  if constexpr (RD) {
     if constexpr (GREEDY) greedy_fold<In>(st.dg, draw, e_base, true, m8);
-    else warm_fold_vs<In, FIRST>(st.dw, draw, c, m8, vs);
-    if constexpr (F > 0) {
-      if (pl.topf) {
-        unsigned bits = 0;
-        constexpr bool have_m8 = FIRST || GREEDY;
-        if constexpr (FIRST) {
-          // at least f vectors reach the f-th largest lane maximum, so every
-          // element of the segment's top-f does; the first chunk's
-          // candidates are the vectors there
-          float lm = m8[0];
+    else warm_fold_vs<In, FIRST>(st.dw, draw, c, m8, vs, d_fixed);
+  }
+  if constexpr (RD && F > 0) {
+    if (pl.topf) {
+      unsigned bits = 0;
+      constexpr bool have_m8 = FIRST || GREEDY;
+      if constexpr (FIRST) {
+        // at least f vectors reach the f-th largest lane maximum, so every
+        // element of the segment's top-f does; the first chunk's
+        // candidates are the vectors there
+        float lm = m8[0];
 #pragma unroll
-          for (int u = 1; u < kU; ++u) lm = fmaxf(lm, m8[u]);
-          st.kv = wave_fth_largest<F>(lm, pl.nf);
+        for (int u = 1; u < kU; ++u) lm = fmaxf(lm, m8[u]);
+        st.kv = wave_fth_largest<F>(lm, pl.nf);
 #pragma unroll
-          for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
-        } else if (!(st.kv > neg_inf())) {
-          bits = (1u << kU) - 1u;  // fewer than f elements seen: all are candidates
-        } else if constexpr (GREEDY) {
+        for (int u = 0; u < kU; ++u) bits |= (m8[u] >= st.kv) ? (1u << u) : 0u;
+        if constexpr (!GREEDY) refresh_eth(st, c);
+      } else if (!(st.kv > neg_inf())) {
+        bits = (1u << kU) - 1u;  // fewer than f elements seen: all are candidates
+      } else if constexpr (GREEDY) {
 #pragma unroll
-          for (int u = 0; u < kU; ++u) bits |= (m8[u] > st.kv) ? (1u << u) : 0u;
-        } else {
-          // an element above kv has a term 2^(x c - hi) of more than
-          // 2^(kv c - hi); a vector whose sum of terms is below that (less a
-          // margin for rounding) holds no such element
-          const float eth = __builtin_amdgcn_exp2f(fmaf(st.kv, c, -st.dw.hi)) * 0.999999f;
+        for (int u = 0; u < kU; ++u) bits |= (m8[u] > st.kv) ? (1u << u) : 0u;
+      } else {
+        // an element above kv has a term 2^(x c - hi) of more than
+        // 2^(kv c - hi) (st.eth, less a margin for rounding); a vector whose
+        // sum of terms is below that holds no such element.  The chunk's
+        // largest vector sum is tested first.
+        if (d_fixed) refresh_eth(st, c);
+        const float vmax = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
+        if (__ballot(vmax >= st.eth)) {
 #pragma unroll
-          for (int u = 0; u < kU; ++u) bits |= (vs[u] >= eth) ? (1u << u) : 0u;
+          for (int u = 0; u < kU; ++u) bits |= (vs[u] >= st.eth) ? (1u << u) : 0u;
         }
-        bits &= (1u << nv) - 1u;  // vectors past the segment belong to the next one
-        if (__ballot(bits != 0u)) {
-          // the maxima are exact where they were computed (first chunk,
-          // temperature 0); elsewhere the candidate is passed on as inexact
-          if constexpr (!have_m8) {
+      }
+      bits &= (1u << nv) - 1u;  // vectors past the segment belong to the next one
+      if (__ballot(bits != 0u)) {
+        // the maxima are exact where they were computed (first chunk,
+        // temperature 0); elsewhere the candidate is passed on as inexact
+        if constexpr (!have_m8) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) m8[u] = neg_inf();
-          }
-          cand_append<F>(L, bits, e_base, SLAB, m8, have_m8, st.nc);
-          if (__ballot(st.nc > kCandSlots - kU))
-            cand_reduce<In, F, 2>(L, drow, V, pl.mask_id, st.nc, st.kv);
+          for (int u = 0; u < kU; ++u) m8[u] = neg_inf();
+        }
+        cand_append<F>(L, bits, e_base, SLAB, m8, have_m8, st.nc);
+        if (__ballot(st.nc > kCandSlots - kU)) {
+          cand_reduce<In, F, 2>(L, drow, V, pl.mask_id, st.nc, st.kv);
+          if constexpr (!GREEDY) refresh_eth(st, c);
         }
       }
     }
@@ -394,6 +413,7 @@ __device__ __forceinline__ void stream_segment(const Params& P, int64_t slot, in
   greedy_init(st.tg); greedy_init(st.dg);
   st.nc = 0;
   st.kv = neg_inf();
+  st.eth = 0.0f;
   if constexpr (F > 0) {
     if (lane == 0) {
 #pragma unroll
@@ -415,6 +435,18 @@ __device__ __forceinline__ void stream_segment(const Params& P, int64_t slot, in
       else stats_segment<In, F, false, true, false>(pl, V, trow, drow, s0, s1, c, st, L, xd, yd);
     }
   }
+  // the output pointers are read from the kernel arguments again, past an
+  // empty asm statement, so that they are not held in scalar registers
+  // while the segment streams (P is the kernel's only argument, at the
+  // start of its argument segment)
+  typedef __attribute__((address_space(4))) const Params KParams;
+  KParams* kp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  Ws WE;
+  WE.cpos = kp->ws.cpos; WE.cvm = kp->ws.cvm; WE.cn = kp->ws.cn;
+  WE.tm = kp->ws.tm; WE.ts = kp->ws.ts; WE.targ = kp->ws.targ;
+  WE.dm = kp->ws.dm; WE.ds = kp->ws.ds; WE.darg = kp->ws.darg;
+  WE.dtv = kp->ws.dtv; WE.dti = kp->ws.dti;
   const int64_t part = slot * kMaxSeg + seg;
   if constexpr (F > 0) {
     if (pl.topf && pl.readD) {
@@ -427,27 +459,27 @@ __device__ __forceinline__ void stream_segment(const Params& P, int64_t slot, in
         incl = 0;
         total = 0;
       }
-      int* dst = W.cpos + part * kDumpCap + (incl - st.nc);
-      float* dvm = W.cvm + part * kDumpCap + (incl - st.nc);
+      int* dst = WE.cpos + part * kDumpCap + (incl - st.nc);
+      float* dvm = WE.cvm + part * kDumpCap + (incl - st.nc);
       for (int i = 0; i < st.nc; ++i) {
         dst[i] = L->pos[i][lane];
         dvm[i] = L->vm[i][lane];
       }
-      if (lane == 0) W.cn[part] = total;
+      if (lane == 0) WE.cn[part] = total;
     }
   }
 
   if (pl.readT) {
     const WaveStats ws = pl.greedy ? wave_finish_greedy(st.tg) : wave_finish_warm(st.tw, c);
-    if (lane == 0) { W.tm[part] = ws.m; W.ts[part] = ws.s; W.targ[part] = ws.arg; }
+    if (lane == 0) { WE.tm[part] = ws.m; WE.ts[part] = ws.s; WE.targ[part] = ws.arg; }
   }
   if (pl.readD) {
     const WaveStats ws = pl.greedy ? wave_finish_greedy(st.dg) : wave_finish_warm(st.dw, c);
-    if (lane == 0) { W.dm[part] = ws.m; W.ds[part] = ws.s; W.darg[part] = ws.arg; }
+    if (lane == 0) { WE.dm[part] = ws.m; WE.ds[part] = ws.s; WE.darg[part] = ws.arg; }
     if constexpr (F > 0) {
       if (pl.topf && lane < F) {
-        W.dtv[part * F + lane] = L->wv[lane];
-        W.dti[part * F + lane] = L->wi[lane];
+        WE.dtv[part * F + lane] = L->wv[lane];
+        WE.dti[part * F + lane] = L->wi[lane];
       }
     }
   }
