@@ -335,6 +335,7 @@ struct DecideLds {
   int hi[kMaxK + 1][2][kMaxF];
   float wv[kDecideWaves][kMaxF];  // split fork blocks: each wave's top-f
   int wi[kDecideWaves][kMaxF];
+  double ct[kTotRegs * kLanes];   // chunk totals, when one block sums the whole row
   int n, status;
 };
 
@@ -685,6 +686,8 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const In* trow = trow_ptr<In>(P, b, jr);
   const In* drow = has_q ? drow_ptr<In>(P, b, jr) : nullptr;
   double* ctr = P.ws.ctr + task * (int64_t)P.cpr;
+  // a row summed by this block alone hands its chunk totals over in LDS
+  const bool in_lds = P.nbs == 1 && P.cpr <= kTotRegs * kLanes;
   {
     constexpr int VEC = Elem<In>::VEC;
     constexpr int64_t SLAB = slab_elems<In>();
@@ -709,7 +712,10 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
     };
     auto sum = [&](const uint4 (&t)[kU], const uint4 (&d)[kU], int ch) {
       const double cr = wave_sum(chunk_rsum<In>(kc, t, d));
-      if (lane == 0) st_dev(ctr + ch, cr);
+      if (lane == 0) {
+        if (in_lds) S.ct[ch] = cr;
+        else st_dev(ctr + ch, cr);
+      }
     };
     if (c0 < c1) {
       load(ta, da, c0);
@@ -724,12 +730,14 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
       }
     }
   }
-  vm_complete();
+  if (!in_lds) vm_complete();
   __syncthreads();
   if (w != 0) return;
-  unsigned* ctr_arrive = (P.mode == kResidual && P.rows_all) ? row_ctr(P.ws, task)
-                                                              : seq_ctr(P.ws, task, kCtrDraw);
-  if (!arrive_last(ctr_arrive, (unsigned)P.nbs)) return;
+  if (!in_lds) {
+    unsigned* ctr_arrive = (P.mode == kResidual && P.rows_all) ? row_ctr(P.ws, task)
+                                                                : seq_ctr(P.ws, task, kCtrDraw);
+    if (!arrive_last(ctr_arrive, (unsigned)P.nbs)) return;
+  }
 
   // 5. the last block: totals (chunk order) and the draw
   double z = 0.0;
@@ -737,7 +745,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
 #pragma unroll
   for (int g = 0; g < kTotRegs; ++g) {
     const int ch = g * kLanes + lane;
-    tc[g] = (ch < P.cpr) ? ld_dev(ctr + ch) : 0.0;
+    tc[g] = (ch < P.cpr) ? (in_lds ? S.ct[ch] : ld_dev(ctr + ch)) : 0.0;
   }
   if (P.cpr <= kTotRegs * kLanes) {
 #pragma unroll
