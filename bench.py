@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--sample", action="store_true",
                     help="instead of the throughput step: the drafter's draw (sv_sample_temp) "
                          "on the 512 draft rows of the batched workload")
+    ap.add_argument("--softmax", action="store_true",
+                    help="time sv_softmax_temp on the batched workload's 512 target rows "
+                         "instead of the verify step")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of the logits' size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -121,6 +124,7 @@ def counter_means(path, counter):
                 continue
             name = r["Kernel_Name"]
             key = ("k_stats" if "sv::k_stats" in name else
+                   "k_decide" if "sv::k_decide" in name else
                    "copy" if "neg_kernel_cuda" in name else None)
             if key is None:
                 continue
@@ -148,6 +152,10 @@ def write_traffic(fetch_csv, write_csv):
            "fetch_kib_raw": fe["k_stats"], "write_kib_raw": wr["k_stats"],
            "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_bytes": copy_bytes}
+    if "k_decide" in fe and "k_decide" in wr:
+        out["k_decide"] = {"fetch_bytes": fe["k_decide"] * 1024.0 * f_scale,
+                           "write_bytes": wr["k_decide"] * 1024.0 * w_scale,
+                           "fetch_kib_raw": fe["k_decide"], "write_kib_raw": wr["k_decide"]}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -337,6 +345,47 @@ def stress(steps, warmup):
                       "moved_GBs": (3 * logits + rows * V * 4) / t2 / 1e9}), flush=True)
 
 
+def softmax_bench(steps, warmup):
+    """sv_softmax_temp on the 512 target rows of the batched Qwen3-vocabulary
+    workload (the workload's temperatures, one per sequence), into a
+    preallocated float32 output: rows/s and algorithmic GB/s (each logit read
+    once, each probability written once)."""
+    import numpy as np
+    import torch
+
+    from verification_sampling_amd import specverify as sv
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[WORKLOAD]
+    w = make_workload(cfg)
+    dev = torch.device("cuda", 0)
+    B, k, V = cfg.B, cfg.k, cfg.V
+    rows = B * (k + 1)
+    x = torch.from_numpy(np.ascontiguousarray(w.target).view(np.int16)).view(
+        torch.bfloat16).reshape(rows, V).to(dev)
+    tau = torch.from_numpy(w.temperature).to(dev)
+    out = torch.empty(rows, V, dtype=torch.float32, device=dev)
+    ws = sv.Workspace(dev)
+    for _ in range(warmup):
+        sv.softmax_temp(x, tau, rows_per_temp=k + 1, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sv.softmax_temp(x, tau, rows_per_temp=k + 1, workspace=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    alg = rows * V * (2 + 4)
+    print(json.dumps({"workload": WORKLOAD + " target rows", "call": "sv_softmax_temp",
+                      "rows": rows, "us_per_call": t * 1e6, "rows_per_s": rows / t,
+                      "alg_bytes": alg, "alg_GBs": alg / t / 1e9,
+                      "frac_of_hbm_peak": alg / t / 8e12,
+                      "bytes_moved": rows * V * (2 + 2 + 4),
+                      "note": "two launches: row statistics (reads the logits), then the "
+                              "normalised rows (reads them again, writes fp32)"}), flush=True)
+
+
 def sample_rows(steps, warmup):
     """sv_sample_temp on the 512 draft rows of the batched Qwen3-vocabulary
     workload (one uniform per row, the workload's temperatures): rows/s and
@@ -375,6 +424,9 @@ def main():
     a = parse()
     if a.sample:
         sample_rows(a.steps, a.warmup)
+        return
+    if a.softmax:
+        softmax_bench(a.steps, a.warmup)
         return
     if a.stress:
         stress(a.steps, a.warmup)
@@ -469,11 +521,24 @@ def main():
     achieved = stats_bytes / stats_avg_s / 1e9
 
     traffic = None
+    decide_traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
         if tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_launch")
+            if "k_decide" in tr:
+                decide_traffic = tr["k_decide"]["fetch_bytes"] + tr["k_decide"]["write_bytes"]
+
+    if a.copy_calib:
+        # counter calibration: a plain copy kernel of known size (reads and
+        # writes total_bytes // 2 bytes once each)
+        x = torch.empty(total_bytes // 8, dtype=torch.float32, device=dev).normal_()
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
 
     # what this GPU reaches on plain HBM traffic of the logits' size: a
     # device-to-device copy (reads and writes every byte), three buffer sets
@@ -521,7 +586,9 @@ def main():
                  "us_median": float(np.median(step_us)),
                  "us_p10": float(np.percentile(step_us, 10)),
                  "us_p90": float(np.percentile(step_us, 90)),
-                 "steps_with_events": int(a.steps)},
+                 "steps_with_events": int(a.steps),
+                 "decide_traffic_bytes": decide_traffic,
+                 "decide_draw_rows_bytes": B * 2 * V * 2},
         "measured_peak": {"d2d_copy_GBs": copy_gbs, "bytes": int(nbytes),
                           "how": "device-to-device copy of a buffer of the step's logits "
                                  "size (bytes read + bytes written per second), three sets "

@@ -454,9 +454,10 @@ def sample_temp(logits, temperature, uniforms, rows_per_temp: int = 1, stream=No
 
 
 def softmax_temp(logits, temperature, rows_per_temp: int = 1,
-                 workspace: Optional[Workspace] = None, stream=None):
+                 workspace: Optional[Workspace] = None, stream=None, out=None):
     """sv_softmax_temp over the rows of a [rows, V] tensor (V contiguous);
-    returns float32 [rows, V]."""
+    returns float32 [rows, V] (written into `out` when given: float32
+    [rows, V], V contiguous, rows 16-byte aligned)."""
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be [rows, V] with V contiguous")
     rows, V = logits.shape
@@ -467,9 +468,13 @@ def softmax_temp(logits, temperature, rows_per_temp: int = 1,
         raise ValueError("temperature must be contiguous float32")
     if temperature.numel() * rows_per_temp < rows:
         raise ValueError("one temperature per rows_per_temp rows is needed")
-    dev = _same_device([logits, temperature], "softmax_temp")
-    Vp = (V + 3) // 4 * 4
-    out = torch.empty(rows, Vp, dtype=torch.float32, device=dev)[:, :V]
+    dev = _same_device([logits, temperature] + ([out] if out is not None else []),
+                       "softmax_temp")
+    if out is None:
+        Vp = (V + 3) // 4 * 4
+        out = torch.empty(rows, Vp, dtype=torch.float32, device=dev)[:, :V]
+    elif (out.dtype != torch.float32 or tuple(out.shape) != (rows, V) or out.stride(1) != 1):
+        raise ValueError(f"out must be float32 [{rows}, {V}] with V contiguous")
     ws = workspace or default_workspace(dev, stream)
     buf = ws.get(workspace_size(rows, 0, V, 0), ("softmax", rows, V), stream)
     code = lib().sv_softmax_temp(
