@@ -140,3 +140,29 @@ def test_cache_hit_checks():
         sv.cache_hit(ft, torch.zeros(B + 1, dtype=torch.int32), torch.zeros(B, dtype=torch.int32))
     with pytest.raises(ValueError, match="ROCm device"):
         sv.cache_hit(ft, torch.zeros(B, dtype=torch.int32), torch.zeros(B, dtype=torch.int32))
+
+
+def test_softmax_checks_its_output():
+    x = torch.zeros(8, 500, dtype=torch.bfloat16)
+    t = torch.ones(8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="out must be"):
+        sv.softmax_temp(x, t, out=torch.zeros(8, 499, dtype=torch.float32))
+    with pytest.raises(ValueError, match="out must be"):
+        sv.softmax_temp(x, t, out=torch.zeros(8, 500, dtype=torch.float16))
+    with pytest.raises(ValueError, match="ROCm device"):
+        sv.softmax_temp(x, t, out=torch.zeros(8, 500, dtype=torch.float32))
+
+
+def test_noalloc_needs_its_outputs():
+    a = good()
+    with pytest.raises(ValueError, match="out"):
+        sv.verify_noalloc(a["target"], a["draft"], a["draft_tokens"], a["temperature"],
+                          a["u_accept"], a["u_recover"], None, f=F)
+    outs = {"accept_len": torch.zeros(B, dtype=torch.int32),
+            "out_token": torch.zeros(B, dtype=torch.int32)}
+    with pytest.raises(ValueError, match="fork_tokens"):
+        sv.verify_noalloc(a["target"], a["draft"], a["draft_tokens"], a["temperature"],
+                          a["u_accept"], a["u_recover"], outs, f=F)
+    with pytest.raises(ValueError, match="ROCm device"):
+        sv.verify_noalloc(a["target"], a["draft"], a["draft_tokens"], a["temperature"],
+                          a["u_accept"], a["u_recover"], outs, f=0)

@@ -468,13 +468,14 @@ def softmax_temp(logits, temperature, rows_per_temp: int = 1,
         raise ValueError("temperature must be contiguous float32")
     if temperature.numel() * rows_per_temp < rows:
         raise ValueError("one temperature per rows_per_temp rows is needed")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (rows, V)
+                            or out.stride(1) != 1):
+        raise ValueError(f"out must be float32 [{rows}, {V}] with V contiguous")
     dev = _same_device([logits, temperature] + ([out] if out is not None else []),
                        "softmax_temp")
     if out is None:
         Vp = (V + 3) // 4 * 4
         out = torch.empty(rows, Vp, dtype=torch.float32, device=dev)[:, :V]
-    elif (out.dtype != torch.float32 or tuple(out.shape) != (rows, V) or out.stride(1) != 1):
-        raise ValueError(f"out must be float32 [{rows}, {V}] with V contiguous")
     ws = workspace or default_workspace(dev, stream)
     buf = ws.get(workspace_size(rows, 0, V, 0), ("softmax", rows, V), stream)
     code = lib().sv_softmax_temp(
