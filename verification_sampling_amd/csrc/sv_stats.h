@@ -297,7 +297,8 @@ __device__ __forceinline__ void cand_append(CandLds<F>* L, unsigned bits, int e_
 // Reduces the slots: re-reads the candidate vectors (NB per round), ranks
 // their elements (id < V, id != mask_id, at or above the lane's running
 // threshold) together with the wave's list, keeps the top-F and raises kv to
-// the F-th once the list is full.  Clears the slots.
+// the list's F-th entry once the list is full (F >= f, so every element of
+// the top-f is at or above it).  Clears the slots.
 template <typename In, int F, int NB>
 __device__ __forceinline__ void cand_reduce(CandLds<F>* L, const In* __restrict__ row, int V,
                                             int mask_id, int& nc, float& kv) {
