@@ -544,3 +544,69 @@ def test_batch_flag_counts():
     np.testing.assert_array_equal(r.flagged, [True, False, True, False])
     assert r.n_flagged_draws == 3
     np.testing.assert_array_equal(r.token, [0, 0, 0, 0])
+
+
+# ---------------------------------------------------------------- small helpers and batch drivers
+
+def test_acceptance_probability_closed_forms():
+    F_ = Fraction
+    assert oracle.acceptance_probability(F_(3, 10), F_(6, 10)) == F_(1, 2)   # p / q below one
+    assert oracle.acceptance_probability(F_(6, 10), F_(3, 10)) == 1          # capped at one
+    assert oracle.acceptance_probability(F_(1, 4), F_(1, 4)) == 1
+    assert oracle.acceptance_probability(F_(1, 5), F_(0)) == 1               # q = 0 < p
+    assert oracle.acceptance_probability(F_(0), F_(0)) == 0                  # p = q = 0
+    assert oracle.acceptance_probability(F_(0), F_(1, 3)) == 0
+    assert oracle.acceptance_probability(0.25, 0.5) == 0.5
+
+
+def test_first_rejection():
+    assert oracle.first_rejection([True, True, False, True]) == 2
+    assert oracle.first_rejection([False, False]) == 0
+    assert oracle.first_rejection([True] * 7) == 7
+    assert oracle.first_rejection([]) == 0
+
+
+def test_argmax_first_is_numpys_first_maximum():
+    rng = np.random.default_rng(70)
+    for _ in range(50):
+        x = rng.integers(0, 5, 40).astype(np.float64)     # many ties
+        assert oracle.argmax_first(x) == int(np.argmax(x))
+    assert oracle.argmax_first(np.array([1.0, 3.0, 3.0, -np.inf])) == 1
+
+
+def test_softmax_rows_per_row_temperatures_and_errors():
+    rng = np.random.default_rng(71)
+    x = (rng.standard_normal((5, 300)) * 2).astype(np.float32)
+    x[3, :] = -np.inf                                     # no finite entry
+    tau = np.array([0.5, 1.0, -1.0, 0.8, np.nan], dtype=np.float32)
+    got = oracle.softmax_rows(x, "f32", tau)
+    for r in (0, 1):
+        np.testing.assert_allclose(got[r], scipy.special.softmax(x[r].astype(np.float64) / tau[r]),
+                                   rtol=1e-13, atol=0)
+    for r in (2, 3, 4):                                  # bad temperature or row
+        assert np.all(np.isnan(got[r]))
+
+
+def test_forked_topf_batch_rows_and_errors():
+    V, k, f = 40, 2, 3
+    rng = np.random.default_rng(72)
+    D = rng.integers(-3, 4, (3, k + 1, V)).astype(np.float32)   # many ties
+    drafts = np.array([[5, 6], [7, 8], [9, V]], dtype=np.int32)  # sequence 2: id out of range
+    tau = np.array([0.7, 0.0, 1.0], dtype=np.float32)
+    toks, probs = oracle.forked_topf_batch(D, "f32", drafts, tau, f)
+    for b in (0, 1):
+        for j in range(k + 1):
+            excl = int(drafts[b, j]) if j < k else None
+            order = sorted((t for t in range(V) if t != excl), key=lambda t: (-D[b, j, t], t))
+            assert list(toks[b, j]) == order[:f], (b, j)
+        if tau[b] == 0:
+            np.testing.assert_array_equal(probs[b][:, 0], 1.0)
+            np.testing.assert_array_equal(probs[b][:, 1:], 0.0)
+        else:
+            for j in range(k + 1):
+                y = D[b, j].astype(np.float64).copy()
+                if j < k:
+                    y[drafts[b, j]] = -np.inf
+                q = scipy.special.softmax(y / tau[b])
+                np.testing.assert_allclose(probs[b, j], q[toks[b, j]], rtol=1e-13)
+    assert np.all(toks[2] == -1) and np.all(np.isnan(probs[2]))
