@@ -14,15 +14,18 @@
 //             rejection by ballot; the owner block writes the outputs; for
 //             temperature > 0 the blocks split row n, sum max(0, p - q) (or
 //             p) per chunk, hand the chunk totals to the last to arrive
-//             (device-scope stores and one arrival counter per sequence),
-//             and that block draws the token by inverse CDF.  Fork blocks
-//             (one per sequence, or one per few rows at small batches) rank
-//             the fork candidates beside them.
-//   k_hits    (forks->hits) the speculation-cache lookup of the outcome.
+//             (device-scope stores and one arrival counter per sequence;
+//             through LDS when one block sums the whole row), and that block
+//             draws the token by inverse CDF.  Fork blocks (one per
+//             sequence, or one per few rows at small batches) rank the fork
+//             candidates beside them.  With forks->hits, whichever of the
+//             draw and the fork ranking finishes second writes the
+//             speculation-cache lookup (no further launch).
 // sv_residual_sample runs k_stats and k_decide at given positions (plus
 // k_write for the full residual distributions); sv_softmax_temp runs
 // k_stats then k_write; sv_forked_topf runs k_stats then k_decide without
-// draws; sv_cache_hit runs k_hits alone.
+// draws; sv_cache_hit runs k_hits, the lookup alone, on forks from another
+// call.
 //
 // The speculative-sampling rule (accept iff u < min(1, p/q), first
 // rejection, draw from max(0, p - q), bonus draw from p_k) follows the
