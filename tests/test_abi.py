@@ -189,3 +189,13 @@ def test_noalloc_scratch_limit_and_validation(L):
     assert call(big, forks=sv.SvForks(3, FAKE, FAKE)) == WORKSPACE
     # the headline batch fits
     assert L.sv_workspace_size(64, 7, 151936, 16) <= sv.NOALLOC_SCRATCH_BYTES
+
+
+def test_batch_limits(L):
+    """B <= 8192 and B * (k + 1) <= 32768 rows per call; at the limits the
+    shape is accepted (the call then fails only on the short workspace)."""
+    V = 64
+    assert call_verify(L, batch(B=8193, k=3, V=V, t_row=V, d_row=V)) == INVALID
+    assert call_verify(L, batch(B=4097, k=7, V=V, t_row=V, d_row=V)) == INVALID   # 32,776 rows
+    assert call_verify(L, batch(B=8192, k=3, V=V, t_row=V, d_row=V), ws_bytes=16) == WORKSPACE
+    assert call_verify(L, batch(B=4096, k=7, V=V, t_row=V, d_row=V), ws_bytes=16) == WORKSPACE

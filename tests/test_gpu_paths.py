@@ -12,6 +12,7 @@
   draw no longer fit the registers of one wave.
 - Residuals of total zero (target and draft rows equal at the drawn
   position), which fall back to the target distribution.
+- The largest batches a call accepts (32,768 rows).
 
 Every comparison is against the oracle on the same inputs; tokens and forks
 exactly, probabilities to 1e-5 relative.
@@ -238,3 +239,25 @@ def test_largest_vocabulary_softmax_and_sampling(sv, dtype):
         if not flagged[r]:
             assert g[r] == ref[r], (r, int(g[r]), int(ref[r]))
     log(f"[paths] largest vocabulary softmax / sampling {dtype}: ok")
+
+
+@pytest.mark.parametrize("B,k", [(4096, 7), (8192, 3)])
+def test_largest_batches(sv, B, k):
+    """The largest batches a call accepts (32,768 rows), at a small
+    vocabulary: every sequence's outputs against the oracle on a sample,
+    and the properties on all."""
+    V, f = 64, 3
+    log(f"[paths] largest batch B={B} k={k} V={V} f={f}")
+    w = make_workload(Config("paths", B=B, k=k, V=V, f=f, dtype="bf16", profile="zipf",
+                             seed=7500 + B, tau_mixed=(0.5, 1.2), sigma_range=(0.3, 1.2)))
+    out = _verify(sv, w.target, w.draft, "bf16", w.draft_tokens, w.temperature, w.u_accept,
+                  w.u_recover, f)
+    al = out["accept_len"].cpu().numpy()
+    assert np.all((al >= 0) & (al <= k))
+    ft = out["fork_tokens"].cpu().numpy()
+    assert np.all((ft >= 0) & (ft < V))
+    seqs = np.arange(0, B, B // 256)
+    ref = oracle_pool.verify_batch(w.target, w.draft, "bf16", w.draft_tokens, w.temperature,
+                                   w.u_accept, w.u_recover, f=f, seqs=seqs)
+    nf, n = compare_verify(out, ref, seqs, f, k)
+    log(f"[paths] largest batch B={B}: compared {n} sequences, flagged {nf}")
