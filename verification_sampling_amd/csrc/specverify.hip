@@ -73,18 +73,33 @@ __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params 
                         &s_cand[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)]);
 }
 
+// Bounds of an inexact candidate's maximum in logits from its key (see
+// inexact_key) and the reciprocal of its scale c: the key's relation
+// widened by a margin for the rounding of the terms, the key and this
+// product.  A key that is not finite bounds nothing.
+template <typename In>
+__device__ __forceinline__ void key_bounds(float key, double inv_c, float& lo, float& hi) {
+  constexpr double kLowBits = (Elem<In>::VEC == 8) ? 4.0 : 3.0;  // 1 + log2(VEC)
+  if (!(finitef(key) && inv_c > 0.0)) { lo = neg_inf(); hi = pos_inf(); return; }
+  const double m = 1e-3 + 1e-5 * fabs((double)key);
+  lo = (float)(((double)key - kLowBits - m) * inv_c);
+  hi = (float)(((double)key + m) * inv_c);
+}
+
 // The candidate vectors the segments of row (b, j) passed on (cnt: this
 // lane's segment's count, lanes < np), a round of 64 * kRound at a time:
-// their positions and maxima are loaded first, and the f-th largest of
-// those maxima (f distinct elements reach it, so it is a lower bound of the
-// row's f-th best) raises the threshold kv.  Only the vectors whose maximum
-// reaches kv, or is unknown (tagged inexact), are re-read; their elements
-// (id < V, id != mask_id) at or above kv go into this lane's list.  With
-// nhalf = 2, two waves share the row: wave `half` takes every other round.
+// their positions and keys are loaded first.  A candidate's key is its
+// maximum, or for an inexact one a key that bounds the maximum from both
+// sides (key_bounds).  The f-th largest of the lower bounds (f distinct
+// elements reach it, so it is a lower bound of the row's f-th best) raises
+// the threshold kv.  Only the vectors whose upper bound reaches kv are
+// re-read; their elements (id < V, id != mask_id) at or above kv go into
+// this lane's list.  With nhalf = 2, two waves share the row: wave `half`
+// takes every other round.
 template <typename In, int F>
 __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, int64_t base,
                                                 int np, int cnt, int mask_id, int half,
-                                                int nhalf, TopList<F>& mine) {
+                                                int nhalf, double cd, TopList<F>& mine) {
   if constexpr (F > 0) {
     constexpr int VEC = Elem<In>::VEC;
     constexpr int kRound = 4;
@@ -94,6 +109,7 @@ __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, i
     const int total = readlane_i(incl, kLanes - 1);
     const In* drow = drow_ptr<In>(P, b, j);
     const int V = P.V;
+    const double inv_c = cd > 0.0 ? 1.0 / cd : 0.0;
     float kv = neg_inf();
     for (int t0 = half * kLanes * kRound; t0 < total; t0 += nhalf * kLanes * kRound) {
       int pos[kRound];
@@ -131,13 +147,17 @@ __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, i
           vm[q] = P.ws.cvm[e];
         }
       }
-      // inexact candidates hold -inf: they add nothing to the bound
-      kv = fmaxf(kv, fth_largest_multi<kRound>(vm, P.f));
+      float lo[kRound], up[kRound];
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
-        const bool inexact = pos[q] >= 0 && (pos[q] & kCandInexact);
+        lo[q] = up[q] = vm[q];
+        if (pos[q] >= 0 && (pos[q] & kCandInexact)) key_bounds<In>(vm[q], inv_c, lo[q], up[q]);
+      }
+      kv = fmaxf(kv, fth_largest_multi<kRound>(lo, P.f));
+#pragma unroll
+      for (int q = 0; q < kRound; ++q) {
         const int p0 = pos[q] >= 0 ? (pos[q] & ~kCandInexact) : -1;
-        const bool keep = p0 >= 0 && (inexact || vm[q] >= kv);
+        const bool keep = p0 >= 0 && up[q] >= kv;
         if (!__ballot(keep)) continue;
         uint4 v = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
                              Elem<In>::kNegInfWord);
@@ -191,7 +211,7 @@ __device__ __forceinline__ void fork_top(const Params& P, int b, int j, const Ro
       for (int r = 0; r < F; ++r) mine.insert(lv[r], li[r]);
     }
     fork_candidates<In, F>(P, b, j, slot_of(P, b, j) * kMaxSeg, P.nparts, cnt, pl.mask_id, half,
-                           nhalf, mine);
+                           nhalf, cd, mine);
     wave_merge_lists<F>(mine, P.f, top);
     float v = neg_inf();
 #pragma unroll

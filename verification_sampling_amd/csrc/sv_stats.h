@@ -261,8 +261,9 @@ __device__ __forceinline__ WaveStats wave_finish_greedy(const Greedy& a) {
 // above kv guarantees.  A candidate lane appends the vector's element index
 // and its maximum to its own slots in LDS; where the maximum was not
 // computed (later chunks at temperature > 0) the index is tagged in its low
-// bit (indices are multiples of the vector width) and the maximum left at
-// -inf.  Nothing else happens while streaming, so the chunk's registers
+// bit (indices are multiples of the vector width) and the maximum replaced
+// by the key of inexact_key, which bounds it from both sides.  Nothing
+// else happens while streaming, so the chunk's registers
 // are free as soon as it is folded.  At the end of the segment the slots
 // are written out, compacted, for the row's ranking; they are reduced in
 // the wave instead (vectors re-read, elements ranked, the wave's top-F kept
@@ -271,10 +272,23 @@ __device__ __forceinline__ WaveStats wave_finish_greedy(const Greedy& a) {
 constexpr int kCandSlots = 16;
 constexpr int kCandInexact = 1;  // tag bit of a candidate whose maximum is unknown
 
+// Key of a vector whose maximum was not computed, from its sum of terms vs
+// = sum_e 2^(x_e c - hi): with vs in [2^(e-1), 2^e) (e its binary exponent),
+// key = e + hi.  Its largest element x_max has a term of at most vs and at
+// least vs / VEC (the other terms are no larger), so
+//   key - 1 - log2(VEC) <= x_max c <= key,
+// up to the rounding of the terms and of the key (a relative 1e-6 or so;
+// the reader adds a margin).  A sum that is zero, subnormal or not finite
+// gives +inf: no bound.
+__device__ __forceinline__ float inexact_key(float vs, float hi) {
+  if (!(vs >= 1.17549435e-38f && vs < pos_inf())) return pos_inf();
+  return (float)__builtin_amdgcn_frexp_expf(vs) + hi;
+}
+
 template <int F>
 struct CandLds {
   int pos[kCandSlots][kLanes];    // element index of each candidate vector (| tag)
-  float vm[kCandSlots][kLanes];   // its maximum, the drafted token masked (-inf if unknown)
+  float vm[kCandSlots][kLanes];   // its maximum, the drafted token masked (inexact: the key)
   float wv[F > 0 ? F : 1];        // the wave's top-F so far (best first)
   int wi[F > 0 ? F : 1];
 };

@@ -331,10 +331,11 @@ __device__ __forceinline__ void stats_chunk(const RowPlan& pl, int V, const In* 
       bits &= (1u << nv) - 1u;  // vectors past the segment belong to the next one
       if (__ballot(bits != 0u)) {
         // the maxima are exact where they were computed (first chunk,
-        // temperature 0); elsewhere the candidate is passed on as inexact
+        // temperature 0); elsewhere the candidate is passed on as inexact,
+        // with the key that bounds its maximum
         if constexpr (!have_m8) {
 #pragma unroll
-          for (int u = 0; u < kU; ++u) m8[u] = neg_inf();
+          for (int u = 0; u < kU; ++u) m8[u] = inexact_key(vs[u], st.dw.hi);
         }
         cand_append<F>(L, bits, e_base, SLAB, m8, have_m8, st.nc);
         if (__ballot(st.nc > kCandSlots - kU)) {
