@@ -359,6 +359,7 @@ struct DecideLds {
   float wv[kDecideWaves][kMaxF];  // split fork blocks: each wave's top-f
   int wi[kDecideWaves][kMaxF];
   double ct[kTotRegs * kLanes];   // chunk totals, when one block sums the whole row
+  ResidCoef kc;                   // coefficients of the row to sum (decision wave)
   int n, status;
 };
 
@@ -668,12 +669,19 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   }
   __syncthreads();
 
-  // 2. decision
+  // 2. decision; for a draw, the decision wave also works out the
+  // coefficients of the row to sum (fp64), once for the block
   if (w == 0) {
     int n, status;
     decide_sequence(P, b, S, sin, owner, n, status);
     if (lane == 0) { S.n = n; S.status = status; }
     if (owner && lane == 0) { P.ws.seqs[b].n = n; P.ws.seqs[b].status = status; }
+    if (status == 2 && P.mode != kForks) {
+      const int jr = (jt >= 0) ? jt : n;
+      const RowStat& R = S.rs[jr];
+      const ResidCoef kc = resid_coef(R.tm, R.ts, R.dm, R.ds, scale_of(tau), jr < P.k);
+      if (lane == 0) S.kc = kc;
+    }
   }
   __syncthreads();
   const int n = S.n;
@@ -704,8 +712,7 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   const bool draw_row = (jt < 0) || (jt == n);
   const bool has_q = jr < P.k;
   const RowStat& R = S.rs[jr];
-  const float c = scale_of(tau);
-  const ResidCoef kc = resid_coef(R.tm, R.ts, R.dm, R.ds, c, has_q);
+  const ResidCoef kc = S.kc;
   const In* trow = trow_ptr<In>(P, b, jr);
   const In* drow = has_q ? drow_ptr<In>(P, b, jr) : nullptr;
   double* ctr = P.ws.ctr + task * (int64_t)P.cpr;
@@ -714,10 +721,9 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   {
     constexpr int VEC = Elem<In>::VEC;
     constexpr int64_t SLAB = slab_elems<In>();
-    const int b0 = (int)((int64_t)part * P.cpr / P.nbs);
-    const int b1 = (int)((int64_t)(part + 1) * P.cpr / P.nbs);
-    const int c0 = b0 + (int)((int64_t)w * (b1 - b0) / kDecideWaves);
-    const int c1 = b0 + (int)((int64_t)(w + 1) * (b1 - b0) / kDecideWaves);
+    // the block's chunks [b0, b1) (32-bit: cpr * nbs is far below 2^31)
+    const int b0 = part * P.cpr / P.nbs;
+    const int b1 = (part + 1) * P.cpr / P.nbs;
     const int64_t slim = (int64_t)P.V / SLAB;
     uint4 ta[kU], da[kU], tb[kU], db[kU];
     auto load = [&](uint4 (&t)[kU], uint4 (&d)[kU], int ch) {
@@ -740,16 +746,23 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
         else st_dev(ctr + ch, cr);
       }
     };
-    if (c0 < c1) {
-      load(ta, da, c0);
-      if (c0 + 1 < c1) load(tb, db, c0 + 1);
-      sum(ta, da, c0);
-      for (int ch = c0 + 1; ch < c1; ch += 2) {
-        if (ch + 1 < c1) load(ta, da, ch + 1);
+    // dealt to the waves in turn (wave w takes b0 + w, b0 + w + 16, ...):
+    // consecutive waves sit on different SIMDs, so a block with fewer
+    // chunks than waves spreads its sums (VALU-heavy: two exponentials per
+    // element) over all four SIMDs.  Each chunk's total does not depend on
+    // which wave sums it.
+    constexpr int kStep = kDecideWaves;
+    int ch = b0 + w;
+    if (ch < b1) {
+      load(ta, da, ch);
+      if (ch + kStep < b1) load(tb, db, ch + kStep);
+      sum(ta, da, ch);
+      for (ch += kStep; ch < b1; ch += 2 * kStep) {
+        if (ch + kStep < b1) load(ta, da, ch + kStep);
         sum(tb, db, ch);
-        if (ch + 1 >= c1) break;
-        if (ch + 2 < c1) load(tb, db, ch + 2);
-        sum(ta, da, ch + 1);
+        if (ch + kStep >= b1) break;
+        if (ch + 2 * kStep < b1) load(tb, db, ch + 2 * kStep);
+        sum(ta, da, ch + kStep);
       }
     }
   }
