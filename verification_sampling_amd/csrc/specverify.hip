@@ -154,20 +154,25 @@ __device__ __forceinline__ void fork_candidates(const Params& P, int b, int j, i
         if (pos[q] >= 0 && (pos[q] & kCandInexact)) key_bounds<In>(vm[q], inv_c, lo[q], up[q]);
       }
       kv = fmaxf(kv, fth_largest_multi<kRound>(lo, P.f));
+      // the round's re-reads are all issued before the first is ranked
+      int p0[kRound];
+      uint4 v[kRound];
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
-        const int p0 = pos[q] >= 0 ? (pos[q] & ~kCandInexact) : -1;
-        const bool keep = p0 >= 0 && up[q] >= kv;
-        if (!__ballot(keep)) continue;
-        uint4 v = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
-                             Elem<In>::kNegInfWord);
-        if (keep) load_vec<In>(drow, p0, V, v);
+        p0[q] = (pos[q] >= 0 && up[q] >= kv) ? (pos[q] & ~kCandInexact) : -1;
+        v[q] = make_uint4(Elem<In>::kNegInfWord, Elem<In>::kNegInfWord, Elem<In>::kNegInfWord,
+                          Elem<In>::kNegInfWord);
+        if (p0[q] >= 0) load_vec<In>(drow, p0[q], V, v[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < kRound; ++q) {
+        if (!__ballot(p0[q] >= 0)) continue;
         float thr = fmaxf(kv, mine.v[F - 1]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float x = elem<In>(v, e);
-          const int id = p0 + e;
-          if (keep && id < V && id != mask_id && x >= thr) {
+          const float x = elem<In>(v[q], e);
+          const int id = p0[q] + e;
+          if (p0[q] >= 0 && id < V && id != mask_id && x >= thr) {
             mine.insert(x, id);
             thr = fmaxf(kv, mine.v[F - 1]);
           }
@@ -1154,9 +1159,9 @@ static hipError_t launch_stats_F(Params& P, hipStream_t s) {
 }
 
 // k_decide: enough blocks per task row to cover the device (one 1024-thread
-// block per CU), at least eight chunks of the summed row per block, plus the
-// fork blocks when verify asks for forks (one per sequence, or up to one per
-// row at small batches).
+// block per CU), at least four chunks of the summed row per block (one
+// chunk sum per SIMD), plus the fork blocks when verify asks for forks (one
+// per sequence, or up to one per row at small batches).
 template <typename In, int F>
 static hipError_t launch_decide_F(Params P, hipStream_t s) {
   const int64_t tasks = (P.mode == kResidual && P.rows_all) ? (int64_t)P.B * (P.k + 1) : P.B;
@@ -1171,7 +1176,7 @@ static hipError_t launch_decide_F(Params P, hipStream_t s) {
   P.fsplit = fsplit;
   const int64_t fork_blocks = forks ? (int64_t)P.B * fsplit : 0;
   int64_t nbs = (device_cus() - fork_blocks) / tasks;
-  nbs = std::max<int64_t>(1, std::min<int64_t>(nbs, std::max<int64_t>(1, P.cpr / 8)));
+  nbs = std::max<int64_t>(1, std::min<int64_t>(nbs, std::max<int64_t>(1, P.cpr / 4)));
   P.nbs = (int32_t)nbs;
   hipLaunchKernelGGL((k_decide<In, F>), dim3((unsigned)(tasks * nbs + fork_blocks)),
                      dim3(kDecideBlock), 0, s, P);
