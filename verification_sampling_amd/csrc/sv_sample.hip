@@ -160,8 +160,9 @@ __global__ __launch_bounds__(kThreads) void k_sample(const In* __restrict__ logi
     return;
   }
 
-  // 2. slab weights relative to the row maximum, scanned in slab order
-  const float hm = M * c;
+  // 2. slab weights relative to the row maximum, scanned in slab order (hm
+  // is M c rounded to fp32, as the slabs' references are)
+  const float hm = __fmul_rn(M, c);
   const double target_u = (double)uniforms[r];
   double Z = 0.0;
   for (int g = 0; g < nslab; g += kLanes) {

@@ -114,6 +114,9 @@ __device__ __noinline__ WarmFix warm_redo(uint4 v0, uint4 v1, uint4 v2, uint4 v3
 #pragma unroll
   for (int u = 0; u < kU; ++u) w.vs[u] = 0.0f;
   if (rn > neg_inf()) {
+    // hn is the new reference exactly as the terms use it (rn c rounded to
+    // fp32): the product is not contracted into the rescaling below
+#pragma clang fp contract(off)
     const float hn = rn * c;
     // old terms 2^(x c - hi) become 2^(x c - hn) = old * 2^(hi - hn)
     if (s > 0.0) w.s = s * (double)__builtin_amdgcn_exp2f(hi - hn);
@@ -219,6 +222,9 @@ struct WaveStats {
 // -hm)), and the factor 2^-lm that makes it relative to M is applied by
 // whoever merges the partials (merge_scale), once per partial.
 __device__ __forceinline__ WaveStats wave_finish_warm(const Warm& a, float c) {
+  // hm must be M c rounded to fp32 (merge_scale corrects for that rounding),
+  // so the product is not contracted into the subtraction
+#pragma clang fp contract(off)
   WaveStats r;
   r.m = wave_max(a.r);
   r.s = 0.0;
