@@ -5,7 +5,7 @@ import it.  The product path (the HIP library and its Python binding) never
 does, and shares no code with it.
 """
 
-from .specverify_oracle import (BF16, F32, FLAG_BAND, BatchResult, ProbVerdict,
+from .specverify_oracle import (BF16, DRAW_ABS_BAND, F32, FLAG_BAND, BatchResult, ProbVerdict,
                                 RowError, SequenceResult,
                                 acceptance_probability, argmax_first,
                                 cache_hit, cache_hits_batch,
@@ -17,7 +17,7 @@ from .specverify_oracle import (BF16, F32, FLAG_BAND, BatchResult, ProbVerdict,
                                 softmax_temp, verify_batch, verify_from_probs,
                                 verify_greedy, verify_sequence, widen)
 
-__all__ = ["BF16", "F32", "FLAG_BAND", "BatchResult", "ProbVerdict",
+__all__ = ["BF16", "DRAW_ABS_BAND", "F32", "FLAG_BAND", "BatchResult", "ProbVerdict",
            "RowError", "SequenceResult", "acceptance_probability",
            "argmax_first", "cache_hit", "cache_hits_batch",
            "first_rejection", "forked_topf",

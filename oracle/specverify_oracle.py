@@ -54,7 +54,13 @@ bonus token from ``p_k``.  Readings of the points the pages leave open:
 8. A draw is flagged when its uniform lies within 1e-6 of a decision
    boundary (the acceptance probability, or a CDF breakpoint of the chosen
    token); a sequence is flagged when any acceptance test up to and including
-   the first rejection, or its final draw, is flagged.
+   the first rejection, or its final draw, is flagged.  The weights of the
+   verify draw are probabilities, or differences of two, that the GPU path
+   holds in fp32, so each cumulative sum is known there only to within
+   2^-23 of the unit probability mass; a verify draw whose target lies that
+   close to a breakpoint is flagged as well (the band is 1e-6 Z + 2^-23 in
+   weight units).  This also flags a residual whose whole mass is below
+   fp32's resolution, which the GPU path sees as zero.
 9. Errors: a temperature that is NaN, negative or infinite, a drafted id
    outside [0, V), or a logits row that is read and whose maximum is not
    finite (+inf, or every entry -inf) make the whole sequence an error.
@@ -76,6 +82,9 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 FLAG_BAND = 1e-6
+# Absolute band of the verify draw, in units of the unit probability mass:
+# the resolution of a cumulative sum of fp32 probabilities (reading 8).
+DRAW_ABS_BAND = 2.0 ** -23
 
 F32 = "f32"
 BF16 = "bf16"
@@ -179,14 +188,15 @@ def residual_weights(P: Sequence, Q: Sequence) -> list:
     return w
 
 
-def inverse_cdf(w: Sequence, u):
+def inverse_cdf(w: Sequence, u, abs_band=0.0):
     """Sample from unnormalised weights w with the uniform u.
 
     Returns (token, flagged).  C_t is the running sum of w in token-id order
     and Z = C_{V-1}; the token is the first t with C_t > u*Z (the running
     sums never decrease, so that is bisect_right); if rounding leaves none,
     the last token of positive weight.  The draw is flagged when u lies
-    within FLAG_BAND of C_{tok-1}/Z or C_tok/Z.
+    within FLAG_BAND + abs_band / Z of C_{tok-1}/Z or C_tok/Z (abs_band in
+    the units of w).
     """
     C = list(itertools.accumulate(w))
     Z = C[-1]
@@ -198,7 +208,7 @@ def inverse_cdf(w: Sequence, u):
         tok = max(t for t, x in enumerate(w) if x > 0)
     lo = C[tok - 1] if tok > 0 else 0 * Z
     hi = C[tok]
-    flagged = min(abs(u - lo / Z), abs(u - hi / Z)) < FLAG_BAND
+    flagged = min(abs(u - lo / Z), abs(u - hi / Z)) < FLAG_BAND + abs_band / Z
     return tok, bool(flagged)
 
 
@@ -234,7 +244,7 @@ def verify_from_probs(P_rows, Q_rows, drafts, u_accept, u_recover) -> ProbVerdic
         flags.append(bool(abs(u_accept[j] - a) < FLAG_BAND))
     n = first_rejection(accepted)
     w = residual_weights(P_rows[n], Q_rows[n]) if n < k else list(P_rows[k])
-    tok, dflag = inverse_cdf(w, u_recover[n])
+    tok, dflag = inverse_cdf(w, u_recover[n], DRAW_ABS_BAND)
     return ProbVerdict(accept_len=n, token=tok, accept_flags=flags,
                        draw_flag=dflag)
 
@@ -409,7 +419,7 @@ def sample_at_position(T, D, dtype, drafts, tau, position, u_recover,
         tok, flag = argmax_first(widen(T[n], dtype)), False
     else:
         w = residual_weights(P[n].tolist(), Q[n].tolist()) if n < k else P[n].tolist()
-        tok, flag = inverse_cdf(w, float(u_recover[n]))
+        tok, flag = inverse_cdf(w, float(u_recover[n]), DRAW_ABS_BAND)
     res = None
     if want_residual:
         res = np.stack([residual_distribution(P[j], Q[j]) for j in range(k)]

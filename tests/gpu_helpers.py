@@ -79,10 +79,11 @@ def assert_flag_share(n_flagged, n_compared, what=""):
         f"{what}: {n_flagged} of {n_compared} flagged (more than {MAX_FLAG_SHARE:.0%})")
 
 
-def compare_verify(out, ref, seqs, f, k, want_p=True, want_q=True):
+def compare_verify(out, ref, seqs, f, k, want_p=True, want_q=True, bound_flags=True):
     """Compares the GPU outputs (full batch) at sequences `seqs` with the
-    oracle's BatchResult over the same sequences, and bounds the share of
-    flagged sequences.  Returns (n_flagged, n_compared)."""
+    oracle's BatchResult over the same sequences, and (unless bound_flags is
+    False, for batches built to be near-uniform) bounds the share of flagged
+    sequences.  Returns (n_flagged, n_compared)."""
     al = out["accept_len"].cpu().numpy()[seqs]
     tok = out["out_token"].cpu().numpy()[seqs]
     n_flag = 0
@@ -111,7 +112,8 @@ def compare_verify(out, ref, seqs, f, k, want_p=True, want_q=True):
             if ref.flagged[i] and not ref.error[i]:
                 continue
             assert hits[i] == ref_hits[i], (int(seqs[i]), int(hits[i]), int(ref_hits[i]))
-    assert_flag_share(n_flag, int((~np.asarray(ref.error)).sum()), "verify")
+    if bound_flags:
+        assert_flag_share(n_flag, int((~np.asarray(ref.error)).sum()), "verify")
     return n_flag, len(seqs)
 
 

@@ -13,6 +13,9 @@
 - Residuals of total zero (target and draft rows equal at the drawn
   position), which fall back to the target distribution.
 - The largest batches a call accepts (32,768 rows).
+- Fork candidates' keys where they are largest (small temperatures, large
+  logits) or crowded within their rounding margin (narrow bands of logits
+  at large temperatures).
 
 Every comparison is against the oracle on the same inputs; tokens and forks
 exactly, probabilities to 1e-5 relative.
@@ -123,6 +126,47 @@ def test_fork_candidates_overflow_long_segments(sv, dtype, B, f):
     assert list(ft[8, 2]) == [int(t) for t in top_ids[1:f + 1]]     # staircase, top_lo drafted
     assert list(ft[16, 0]) == list(range(20001, 20001 + f))
     log(f"[paths] candidate overflow {dtype}: compared {n} sequences, flagged {nf}")
+
+
+# (scale of the logits, offset, temperature) per sequence: keys largest
+# (small temperatures, logits of large magnitude, a large offset that makes
+# the reference large), keys crowded within their margin (a narrow band of
+# logits at large temperatures), and ordinary rows between them
+_KEY_CASES = [(40.0, 0.0, 0.02), (40.0, 0.0, 0.05), (40.0, 0.0, 0.1), (40.0, 0.0, 0.3),
+              (1e-3, 0.0, 4.0), (1e-3, 0.0, 20.0), (1e-3, 0.0, 0.7), (1e-3, 0.0, 100.0),
+              (1.0, 0.0, 0.7), (1.0, 0.0, 0.0), (1.0, 0.0, 1.5), (1.0, 0.0, 0.05),
+              (1.0, 1000.0, 0.05), (1.0, 1000.0, 0.7), (1.0, -1000.0, 0.3), (4.0, 500.0, 0.02)]
+
+
+@pytest.mark.parametrize("dtype,f", [("bf16", 3), ("f32", 3), ("bf16", 16)])
+def test_fork_candidate_keys_at_extreme_scales(sv, dtype, f):
+    """Later-chunk fork candidates at temperature > 0 carry a key that bounds
+    their maximum from both sides, widened by a rounding margin; a margin
+    too tight would skip a vector that holds one of the top f.  Whole
+    batches at the scales where the keys are largest or most crowded."""
+    B, k, V = len(_KEY_CASES), 3, 151936
+    log(f"[paths] fork keys {dtype} B={B} k={k} V={V} f={f}")
+    w = make_workload(Config("keys", B=B, k=k, V=V, f=f, dtype=dtype, profile="zipf",
+                             seed=7300 + f + (dtype == "f32"), tau=0.7,
+                             sigma_range=(0.3, 1.2)))
+    T, D = w.target.copy(), w.draft.copy()
+    tau = np.empty(B, np.float32)
+    for b, (scale, offset, t) in enumerate(_KEY_CASES):
+        for X in (T, D):
+            x = oracle.widen(X[b], dtype) * scale + offset
+            X[b] = _store(x.astype(np.float32), dtype)
+        tau[b] = t
+    out = _verify(sv, T, D, dtype, w.draft_tokens, tau, w.u_accept, w.u_recover, f)
+    ref = oracle.verify_batch(T, D, dtype, w.draft_tokens, tau, w.u_accept, w.u_recover, f=f)
+    # Forks and their probabilities are compared for every sequence.  These
+    # rows flag many draws on purpose: near-uniform rows put a draw inside
+    # the 1e-6 band of a CDF step about a third of the time, and at the
+    # smallest temperatures target and draft agree so closely that the
+    # residual's mass falls below the fp32 resolution band of the draw.  So
+    # the flagged share is bounded at a quarter here, not 5 %.
+    nf, n = compare_verify(out, ref, np.arange(B), f, k, bound_flags=False)
+    assert nf <= B // 4, np.flatnonzero(ref.flagged)
+    log(f"[paths] fork keys {dtype} f={f}: compared {n} sequences, flagged {nf}")
 
 
 @pytest.mark.parametrize("dtype,V", [("f32", 300000), ("bf16", 600000), ("f32", MAX_V)])

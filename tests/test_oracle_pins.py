@@ -515,6 +515,38 @@ def test_draw_flag_flags_the_sequence():
     assert not v.draw_flag and not v.flagged
 
 
+def test_draw_flag_absolute_band():
+    """The verify draw's band adds 2^-23 of the unit probability mass (the
+    resolution of a cumulative sum of fp32 probabilities) to 1e-6 Z.  Unit
+    mass (1/2, 1/2): 1e-6 + 1.2e-7 around 1/2.  Mass 1/100 (1/200, 1/200):
+    the absolute part is 1.2e-5 in units of Z.  The plain inverse CDF (no
+    absolute band) keeps 1e-6."""
+    band = oracle.DRAW_ABS_BAND
+    assert band == 2.0 ** -23
+    w = [0.5, 0.5]
+    assert oracle.inverse_cdf(w, 0.5 + 1.05e-6, band) == (1, True)
+    assert oracle.inverse_cdf(w, 0.5 + 1.05e-6) == (1, False)
+    assert oracle.inverse_cdf(w, 0.5 + 1.2e-6, band) == (1, False)
+    w = [0.005, 0.005]
+    assert oracle.inverse_cdf(w, 0.5 + 1e-5, band) == (1, True)
+    assert oracle.inverse_cdf(w, 0.5 + 1.5e-5, band) == (1, False)
+
+
+def test_residual_below_fp32_resolution_is_flagged():
+    """p_0 and q_0 agree on token 0 up to 1e-60: the residual (0, 1e-60, 0)
+    is exact and positive, the rejection at 0 draws token 1 from it, and
+    the draw is flagged (fp32 weights cannot hold that mass).  With a
+    residual mass of 1/4 the same draw is clean."""
+    F_ = Fraction
+    Q = [[F_(1), F_(0), F_(0)]]
+    for mass, flagged in [(F_(1, 10**60), True), (F_(1, 4), False)]:
+        P = [[1 - mass, mass, F_(0)], [F_(1, 3)] * 3]
+        v = oracle.verify_from_probs(P, Q, [2], [F_(1, 2)], [F_(1, 2), F_(1, 2)])
+        assert v.accept_len == 0 and v.token == 1
+        assert v.accept_flags == [False]
+        assert v.draw_flag == flagged and v.flagged == flagged
+
+
 def test_batch_flag_counts():
     """The batch driver's counts, worked by hand on four sequences built from
     logits with exact probabilities (V = 2, tau = 1): target rows (0, 0)
