@@ -63,6 +63,7 @@ template <typename In, int F>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_PER_EU))) void k_stats(Params P) {
   __shared__ CandLds<F> s_cand[kWavesPerBlock];
+  warm_kernargs();
   const int64_t task = wave_global_id();
   if (task >= P.nslots * P.nparts) return;
   const int64_t slot = task / P.nparts;
@@ -510,6 +511,7 @@ __device__ __forceinline__ void hit_input_ready(const Params& P, int b) {
 template <typename In, int F>
 __global__ __launch_bounds__(kDecideBlock) void k_decide(Params P) {
   __shared__ DecideLds S;
+  warm_kernargs();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int K1 = P.k + 1;

@@ -121,6 +121,19 @@ struct Params {
   Ws ws;
 };
 
+// Touches every 64-byte line of the kernel's argument block with scalar
+// loads issued together, so that the argument loads the code makes later,
+// some of them only after earlier ones return, find the lines in the
+// scalar cache.
+__device__ __forceinline__ void warm_kernargs() {
+  typedef __attribute__((address_space(4))) const uint32_t KWord;
+  KWord* kp = (KWord*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t acc = 0;
+#pragma unroll
+  for (int off = 0; off < (int)sizeof(Params); off += 64) acc |= kp[off / 4];
+  asm volatile("" ::"s"(acc));
+}
+
 __device__ __forceinline__ bool tau_ok(float t) { return t >= 0.0f && t < pos_inf(); }
 
 __device__ __forceinline__ float slot_tau(const Params& P, int64_t slot, int b) {
