@@ -855,15 +855,38 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
   const float nan = __uint_as_float(0x7fc00000u);
 
   int b, j;
+  float tau;
+  if (P.mode == kSoftmax) {
+    b = (int)slot; j = 0;
+    tau = P.tau[slot / P.rows_per_temp];
+  } else {
+    b = (int)(slot / (P.k + 1));
+    j = (int)(slot - (int64_t)b * (P.k + 1));
+    tau = P.tau[b];
+  }
+  b = uniform(b); j = uniform(j);
+  const int64_t sl = (int64_t)chunk * kU;
+  const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
+  const bool full = sl + kU <= (int64_t)P.V / SLAB;
+  const int eb = (int)(sl * SLAB) + lane * VEC;
+  // the chunk's loads go out before the row's statistics are merged or
+  // read (they do not depend on them), whenever the temperature asks for
+  // values
+  const bool has_q = (P.mode == kResidual) && j < P.k;
+  uint4 traw[kU], draw[kU];
+  if (tau > 0.0f && tau_ok(tau)) {
+    const In* tr = (P.mode == kSoftmax) ? reinterpret_cast<const In*>(P.T) + slot * P.t_row
+                                        : trow_ptr<In>(P, b, j);
+    load_chunk<In>(tr, eb, nv, P.V, full, traw);
+    if (has_q) load_chunk<In>(drow_ptr<In>(P, b, j), eb, nv, P.V, full, draw);
+  }
+
   float* orow;
   int state;  // 0 NaN, 1 one-hot, 2 values
-  float tau;
   float tm, dm = 0.0f;
   double ts, ds = 1.0, zr = 0.0;
   int targ;
   if (P.mode == kSoftmax) {
-    b = (int)slot; j = 0;
-    tau = P.tau[slot / P.rows_per_temp];
     orow = P.out + slot * P.out_row;
     const bool greedy = tau == 0.0f || !tau_ok(tau);
     const Merged t = merge_partials(P.ws.tm, P.ws.ts, P.ws.targ, slot * kMaxSeg, P.nparts, greedy,
@@ -871,9 +894,6 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
     tm = t.m; ts = t.s; targ = t.arg;
     state = (!tau_ok(tau) || !finitef(t.m)) ? 0 : (tau == 0.0f ? 1 : 2);
   } else {
-    b = (int)(slot / (P.k + 1));
-    j = (int)(slot - (int64_t)b * (P.k + 1));
-    tau = P.tau[b];
     orow = P.out + (int64_t)b * P.out_seq + (int64_t)j * P.out_row;
     const int st = P.ws.seqs[b].status;
     state = (st == 0) ? 0 : (tau == 0.0f ? 1 : 2);
@@ -889,25 +909,15 @@ __global__ __launch_bounds__(kBlock) void k_write(Params P) {
       tm = t.m; ts = t.s; targ = t.arg;
     }
   }
-  b = uniform(b); j = uniform(j); state = uniform(state);
-  const int64_t sl = (int64_t)chunk * kU;
-  const int nv = (int)min<int64_t>(kU, (int64_t)P.nslab - sl);
-  const bool full = sl + kU <= (int64_t)P.V / SLAB;
-  const int eb = (int)(sl * SLAB) + lane * VEC;
+  state = uniform(state);
 
-  uint4 traw[kU], draw[kU];
   ResidCoef kc;
   float inv_z = 1.0f;
   bool use_r = false;
   if (state == 2) {
-    const bool has_q = (P.mode == kResidual) && j < P.k;
     kc = resid_coef(tm, ts, dm, ds, scale_of(tau), has_q);
     use_r = has_q && zr > 0.0;
     if (use_r) inv_z = (float)(1.0 / zr);
-    const In* tr = (P.mode == kSoftmax) ? reinterpret_cast<const In*>(P.T) + slot * P.t_row
-                                        : trow_ptr<In>(P, b, j);
-    load_chunk<In>(tr, eb, nv, P.V, full, traw);
-    if (has_q) load_chunk<In>(drow_ptr<In>(P, b, j), eb, nv, P.V, full, draw);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
